@@ -1,0 +1,263 @@
+"""Pins of the oracle's SwiGLU, scaled/grouped GEMMs and group padding against
+torch CPU float64 routines (silu, autograd), exact rational brute force,
+lossless-quantization identities and hand-worked padding examples."""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mx
+from quantize_grouped_gemm_amd import synth
+
+GOLDEN_PAD = os.path.join(os.path.dirname(__file__), "golden", "pad_groups.json")
+
+
+# ---------------------------------------------------------------- SwiGLU
+
+def _ab(shape, seed, scale=3.0):
+    g = synth.generator(seed)
+    a = synth.normal_bf16(shape, scale, g)
+    b = synth.normal_bf16(shape, scale, g)
+    dh = synth.normal_bf16(shape, 1.0, g)
+    return synth.bits(a), synth.bits(b), synth.bits(dh)
+
+
+def test_swiglu_forward_matches_torch_silu():
+    a, b, _ = _ab((64, 128), 1)
+    af, bf = mx.bf16_to_f64(a), mx.bf16_to_f64(b)
+    ref = (torch.nn.functional.silu(torch.from_numpy(af)) * torch.from_numpy(bf)).numpy()
+    np.testing.assert_allclose(mx.swiglu_f64(af, bf), ref, rtol=1e-15, atol=0)
+
+
+def test_swiglu_special_cases():
+    a = np.array([0.0, -1000.0, 1000.0, 2.5, -2.5, 1e-30])
+    b = np.array([7.0, 3.0, 3.0, 1.0, 1.0, 1.0])
+    h = mx.swiglu_f64(a, b)
+    assert h[0] == 0.0 and h[1] == 0.0 and h[2] == 3000.0
+    assert mx.swiglu_f64(np.array([1.7]), np.array([0.0]))[0] == 0.0
+    # silu(a) - silu(-a) = a
+    np.testing.assert_allclose(h[3] - h[4], 2.5, rtol=1e-15)
+    np.testing.assert_allclose(h[5], 0.5e-30, rtol=1e-15)
+
+
+def test_swiglu_backward_matches_torch_autograd():
+    a, b, dh = _ab((32, 96), 2)
+    at = torch.from_numpy(mx.bf16_to_f64(a)).requires_grad_()
+    bt = torch.from_numpy(mx.bf16_to_f64(b)).requires_grad_()
+    dht = torch.from_numpy(mx.bf16_to_f64(dh))
+    (torch.nn.functional.silu(at) * bt * dht).sum().backward()
+    da, db = mx.swiglu_grad_f64(dht.numpy(), at.detach().numpy(), bt.detach().numpy())
+    np.testing.assert_allclose(da, at.grad.numpy(), rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(db, bt.grad.numpy(), rtol=1e-13, atol=1e-300)
+
+
+def test_swiglu_quant_outputs_layout():
+    a, b, dh = _ab((64, 96), 3)
+    f = mx.swiglu_quant_fwd(a, b, "rceil")
+    assert f["q_row"].shape == (64, 96) and f["s_row"].shape == (64, 3)
+    assert f["q_col"].shape == (96, 64) and f["s_col"].shape == (96, 2)
+    r = mx.swiglu_quant_bwd(dh, a, b, "floor")
+    assert r["q_row"].shape == (64, 192) and r["q_col"].shape == (192, 64)
+    # the bf16 results dequantize back within half an E4M3 step per element
+    d = mx.dequantize(r["q_row"], r["s_row"])
+    v = mx.bf16_to_f64(r["dab"])
+    assert np.all(np.abs(d - v) <= np.abs(v) / 8 + 2.0 ** -140 + np.repeat(
+        np.exp2(r["s_row"].astype(float) - 127 - 9), 32, axis=-1))
+
+
+# ---------------------------------------------------------------- GEMMs
+
+def _rand_mx(rows, cols, seed, code_max=0x7E, scale_lo=110, scale_hi=140):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, code_max + 1, (rows, cols)) | (rng.integers(0, 2, (rows, cols)) << 7)
+    s = rng.integers(scale_lo, scale_hi, (rows, cols // 32))
+    return q.astype(np.uint8), s.astype(np.uint8)
+
+
+def _exact_value(code, scale):
+    """E4M3 code * 2**(scale-127) as an exact Fraction, from the bit fields."""
+    code = int(code)
+    sign = -1 if code & 0x80 else 1
+    e, m = (code >> 3) & 0xF, code & 7
+    mag = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+    return sign * mag * Fraction(2) ** (int(scale) - 127)
+
+
+def test_scaled_mm_equals_exact_rational_sum():
+    # narrow scale spread: every partial sum fits float64's 53 bits, so the
+    # float64 result must equal the exact rational sum
+    qa, sa = _rand_mx(3, 64, 1, scale_lo=125, scale_hi=130)
+    qb, sb = _rand_mx(4, 64, 2, scale_lo=125, scale_hi=130)
+    got = mx.scaled_mm(qa, sa, qb, sb)
+    for m in range(3):
+        for n in range(4):
+            exact = sum(_exact_value(qa[m, k], sa[m, k // 32]) * _exact_value(qb[n, k], sb[n, k // 32])
+                        for k in range(64))
+            assert Fraction(got[m, n]) == exact
+    # wide spread: within the float64 summation bound K * 2**-53 * sum |terms|
+    qa, sa = _rand_mx(3, 64, 3)
+    qb, sb = _rand_mx(4, 64, 4)
+    got = mx.scaled_mm(qa, sa, qb, sb)
+    for m in range(3):
+        for n in range(4):
+            terms = [_exact_value(qa[m, k], sa[m, k // 32]) * _exact_value(qb[n, k], sb[n, k // 32])
+                     for k in range(64)]
+            bound = 64 * Fraction(2) ** -53 * sum(abs(t) for t in terms)
+            assert abs(Fraction(got[m, n]) - sum(terms)) <= bound
+
+
+def test_scaled_mm_unit_scales_small_integers_exact():
+    rng = np.random.default_rng(3)
+    vals = np.array([0.0, 1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0, 8.0, -1.0, -3.0, -8.0])
+    A = rng.choice(vals, (16, 128))
+    B = rng.choice(vals, (8, 128))
+    qa = mx.e4m3_encode(A)
+    qb = mx.e4m3_encode(B)
+    one = np.full((16, 4), 127, np.uint8)
+    got = mx.scaled_mm(qa, one, qb, one[:8])
+    np.testing.assert_array_equal(got, A @ B.T)
+    assert np.all(got == np.round(got))
+
+
+def _grid_tensor(rows, cols, seed):
+    """Values already on the MXFP8 grid in both directions: E4M3 values with
+    one +-448 in every 32-block of every row and every column, so RCEIL gives
+    scale 1 and quantization is lossless row-wise and column-wise."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 0x7E, (rows, cols)) | (rng.integers(0, 2, (rows, cols)) << 7)
+    v = mx.E4M3_VALUES[codes]
+    r, c = np.indices((rows, cols))
+    v = np.where((r + c) % 32 == 0, np.where(codes & 0x80, -448.0, 448.0), v)
+    return v
+
+
+def _q(v, axis_last=True):
+    q, s = mx.quantize(v if axis_last else v.T, "rceil")
+    np.testing.assert_array_equal(mx.dequantize(q, s), v if axis_last else v.T)
+    return q, s
+
+
+def test_grouped_gemms_match_torch_autograd_on_lossless_inputs():
+    """Forward, input gradient and weight gradient of y_g = x_g W_g^T per
+    group equal torch float64 autograd when quantization is lossless."""
+    E, N, K, Tcap = 3, 64, 96, 384
+    offs = np.array([128, 128, 320], np.int32)        # group 1 empty, tail [320, 384)
+    x = _grid_tensor(Tcap, K, 1)
+    w = np.stack([_grid_tensor(N, K, 10 + g) for g in range(E)])
+    dy = _grid_tensor(Tcap, N, 2)
+    x[320:] = 0.0
+    dy[320:] = 0.0
+    qx, sx = _q(x)
+    qw, sw = zip(*[_q(w[g]) for g in range(E)])
+    y = mx.grouped_mm(qx, sx, np.stack(qw), np.stack(sw), offs)
+    qdy, sdy = _q(dy)
+    qwt, swt = zip(*[_q(w[g], axis_last=False) for g in range(E)])  # W^T [K, N] along N
+    dx = mx.grouped_mm(qdy, sdy, np.stack(qwt), np.stack(swt), offs)
+    qdyT, sdyT = _q(dy, axis_last=False)
+    qxT, sxT = _q(x, axis_last=False)
+    dw = mx.grouped_mm_wgrad(qdyT, sdyT, qxT, sxT, offs)
+
+    xt = torch.from_numpy(x).requires_grad_()
+    wt = torch.from_numpy(w).requires_grad_()
+    bounds = [(0, 128), (128, 128), (128, 320)]
+    ys = [xt[s:e] @ wt[g].T for g, (s, e) in enumerate(bounds)]
+    yt = torch.cat(ys + [torch.zeros(Tcap - 320, N, dtype=torch.float64)])
+    yt.backward(torch.from_numpy(dy))
+    np.testing.assert_allclose(y, yt.detach().numpy(), rtol=1e-14, atol=1e-9)
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-14, atol=1e-9)
+    np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=1e-14, atol=1e-9)
+    assert np.all(y[320:] == 0) and np.all(dw[1] == 0)
+
+
+def test_grouped_mm_rowwise_bruteforce():
+    E, N, K, Tcap = 4, 8, 64, 256
+    offs = np.array([32, 32, 160, 224], np.int32)
+    qa, sa = _rand_mx(Tcap, K, 4)
+    qw = np.stack([_rand_mx(N, K, 20 + g)[0] for g in range(E)])
+    sw = np.stack([_rand_mx(N, K, 20 + g)[1] for g in range(E)])
+    got = mx.grouped_mm(qa, sa, qw, sw, offs)
+    A = mx.dequantize(qa, sa)
+    for r in range(Tcap):
+        g = int(np.searchsorted(offs, r, side="right"))
+        if g >= E:
+            assert np.all(got[r] == 0)
+            continue
+        W = mx.dequantize(qw[g], sw[g])
+        for n in range(N):
+            assert got[r, n] == pytest.approx(float(np.dot(A[r], W[n])), rel=1e-14, abs=1e-300)
+
+
+def test_wgrad_bruteforce_and_hp():
+    N, K, Tcap = 8, 16, 192
+    offs = np.array([0, 64, 192], np.int32)
+    qg, sg = _rand_mx(N, Tcap, 5)
+    qx, sx = _rand_mx(K, Tcap, 6)
+    got = mx.grouped_mm_wgrad(qg, sg, qx, sx, offs)
+    G, X = mx.dequantize(qg, sg), mx.dequantize(qx, sx)
+    assert np.all(got[0] == 0)
+    for g, (s, e) in enumerate([(0, 0), (0, 64), (64, 192)]):
+        for n in range(N):
+            for k in range(K):
+                ref = sum(G[n, t] * X[k, t] for t in range(s, e))
+                assert got[g, n, k] == pytest.approx(ref, rel=1e-13, abs=1e-300)
+    # wgrad_with_hp: bf16 operands, per-group G^T X, checked against torch
+    gb = synth.bits(synth.normal_bf16((Tcap, N), 1.0, synth.generator(7)))
+    xb = synth.bits(synth.normal_bf16((Tcap, K), 1.0, synth.generator(8)))
+    hp = mx.grouped_mm_wgrad_hp(gb, xb, offs)
+    gt = torch.from_numpy(mx.bf16_to_f64(gb))
+    xt = torch.from_numpy(mx.bf16_to_f64(xb))
+    np.testing.assert_allclose(hp[2], (gt[64:192].T @ xt[64:192]).numpy(), rtol=1e-13)
+    assert np.all(hp[0] == 0)
+
+
+def test_single_group_equals_dense_and_bad_offsets_raise():
+    qa, sa = _rand_mx(128, 64, 9)
+    qb, sb = _rand_mx(16, 64, 10)
+    one = mx.grouped_mm(qa, sa, qb[None], sb[None], np.array([128]))
+    np.testing.assert_array_equal(one, mx.scaled_mm(qa, sa, qb, sb))
+    with pytest.raises(ValueError):
+        mx.grouped_mm(qa, sa, qb[None], sb[None], np.array([160]))
+    with pytest.raises(ValueError):
+        mx.grouped_mm(qa, sa, np.stack([qb, qb]), np.stack([sb, sb]), np.array([64, 32]))
+
+
+# ---------------------------------------------------------------- padding
+
+def test_pad_golden_examples():
+    with open(GOLDEN_PAD) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        sizes = np.array(c["sizes"])
+        T = int(sizes.sum())
+        x = (np.arange(T, dtype=np.uint16) + 1)[:, None] * np.ones((1, 4), np.uint16)
+        x_pad, offs, src = mx.pad_groups(x, sizes, c["multiple"], c["capacity"])
+        assert offs.tolist() == c["offs"]
+        real = [r for r in range(c["capacity"]) if src[r] >= 0]
+        assert [int(src[r]) for r in real] == list(range(T))
+        for r in range(c["capacity"]):
+            if src[r] < 0:
+                assert np.all(x_pad[r] == 0)
+            else:
+                assert np.all(x_pad[r] == src[r] + 1)
+        assert c["first_rows"] == [int(src[o]) for o in [0] + c["offs"][:-1] if o < c["capacity"]]
+        np.testing.assert_array_equal(mx.unpad_groups(x_pad, src, T), x)
+
+
+def test_pad_invariants_random_and_errors():
+    for seed in range(5):
+        sizes = synth.dirichlet_group_sizes(3000, 12, 0.3, seed)
+        Tcap = synth.capacity(3000, 12)
+        x = np.random.default_rng(seed).integers(0, 1 << 16, (3000, 8)).astype(np.uint16)
+        x_pad, offs, src = mx.pad_groups(x, sizes, 128, Tcap)
+        assert np.all(offs % 128 == 0) and np.all(np.diff(np.r_[0, offs]) >= sizes)
+        assert np.all(np.diff(np.r_[0, offs]) - sizes < 128) and offs[-1] <= Tcap
+        assert (src >= 0).sum() == 3000
+        np.testing.assert_array_equal(mx.unpad_groups(x_pad, src, 3000), x)
+    with pytest.raises(ValueError):
+        mx.pad_groups(np.zeros((10, 4), np.uint16), np.array([5, 6]), 128, 256)
+    with pytest.raises(ValueError):
+        mx.pad_groups(np.zeros((300, 4), np.uint16), np.array([100, 100, 100]), 128, 256)
