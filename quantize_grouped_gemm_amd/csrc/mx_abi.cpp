@@ -1,0 +1,305 @@
+// C ABI of libmxfp8.so (declared and documented in include/mxfp8.h):
+// argument validation on the host, device check, and kernel launch on the
+// caller's stream. Nothing here reads device memory or synchronizes.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/mxfp8.h"
+#include "mx_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mx_status fail(mx_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// 0 = unknown, 1 = gfx950, -1 = other
+int g_dev_ok[64];
+
+mx_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0)
+    return fail(MX_ERR_DEVICE, "no HIP device (%s)", hipGetErrorString(e));
+  if (dev < 64 && g_dev_ok[dev] == 1) return MX_OK;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(MX_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_dev_ok[dev] = ok ? 1 : -1;
+  if (!ok) return fail(MX_ERR_DEVICE, "device %d is %s; libmxfp8 runs on gfx950 only", dev, prop.gcnArchName);
+  return MX_OK;
+}
+
+mx_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MX_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+#define MX_REQUIRE(cond, st, ...) \
+  do {                            \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+#define MX_DEVICE()                          \
+  do {                                       \
+    mx_status st_ = check_device();          \
+    if (st_ != MX_OK) return st_;            \
+  } while (0)
+
+extern "C" {
+
+int mx_abi_version(void) { return 1; }
+
+const char* mx_last_error(void) { return g_err; }
+
+mx_status mx_init(void) { return check_device(); }
+
+mx_status mx_quantize(const void* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
+                      mx_scale_mode mode, unsigned dirs, uint8_t* q_row, uint8_t* s_row,
+                      uint8_t* q_col, uint8_t* s_col, void* stream) {
+  MX_REQUIRE(mode == MX_RCEIL || mode == MX_FLOOR, MX_ERR_ARG, "mx_quantize: bad scale mode %d", (int)mode);
+  MX_REQUIRE(dirs != 0 && (dirs & ~3u) == 0, MX_ERR_ARG, "mx_quantize: dirs must be MX_ROWWISE|MX_COLWISE");
+  MX_REQUIRE(batch >= 0 && rows >= 0 && cols >= 0, MX_ERR_SHAPE, "mx_quantize: negative size");
+  MX_REQUIRE(cols % 32 == 0, MX_ERR_SHAPE, "mx_quantize: cols (%lld) must be a multiple of 32", (long long)cols);
+  MX_REQUIRE(!(dirs & MX_COLWISE) || rows % 32 == 0, MX_ERR_SHAPE,
+             "mx_quantize: column-wise needs rows (%lld) to be a multiple of 32", (long long)rows);
+  MX_REQUIRE(ld >= cols && ld % 8 == 0, MX_ERR_ALIGN, "mx_quantize: ld (%lld) must be >= cols and a multiple of 8", (long long)ld);
+  MX_REQUIRE((rows + 127) / 128 <= 65535 && batch <= 65535, MX_ERR_SHAPE, "mx_quantize: too many rows or matrices for one launch");
+  if (batch == 0 || rows == 0 || cols == 0) return MX_OK;
+  MX_REQUIRE(x, MX_ERR_NULL, "mx_quantize: x is NULL");
+  MX_REQUIRE(al16(x), MX_ERR_ALIGN, "mx_quantize: x must be 16-byte aligned");
+  if (dirs & MX_ROWWISE) {
+    MX_REQUIRE(q_row && s_row, MX_ERR_NULL, "mx_quantize: q_row/s_row NULL");
+    MX_REQUIRE(al16(q_row), MX_ERR_ALIGN, "mx_quantize: q_row must be 16-byte aligned");
+  }
+  if (dirs & MX_COLWISE) {
+    MX_REQUIRE(q_col && s_col, MX_ERR_NULL, "mx_quantize: q_col/s_col NULL");
+    MX_REQUIRE(al16(q_col), MX_ERR_ALIGN, "mx_quantize: q_col must be 16-byte aligned");
+  }
+  MX_DEVICE();
+  mxk::QuantArgs a{static_cast<const uint16_t*>(x), rows, cols, ld, mode == MX_RCEIL,
+                   (dirs & MX_ROWWISE) ? q_row : nullptr, (dirs & MX_ROWWISE) ? s_row : nullptr,
+                   (dirs & MX_COLWISE) ? q_col : nullptr, (dirs & MX_COLWISE) ? s_col : nullptr};
+  return launched(mxk::launch_quant(a, batch, as_stream(stream)), "mx_quantize");
+}
+
+mx_status mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols,
+                        mx_dtype out_dtype, void* out, void* stream) {
+  MX_REQUIRE(out_dtype == MX_BF16 || out_dtype == MX_F32, MX_ERR_ARG, "mx_dequantize: bad dtype");
+  MX_REQUIRE(rows >= 0 && cols >= 0 && cols % 32 == 0, MX_ERR_SHAPE, "mx_dequantize: cols must be a multiple of 32");
+  if (rows == 0 || cols == 0) return MX_OK;
+  MX_REQUIRE(q && s && out, MX_ERR_NULL, "mx_dequantize: NULL pointer");
+  MX_REQUIRE(al16(q) && al16(out), MX_ERR_ALIGN, "mx_dequantize: q/out must be 16-byte aligned");
+  MX_DEVICE();
+  mxk::DequantArgs a{q, s, rows, cols, out_dtype == MX_F32, out};
+  return launched(mxk::launch_dequant(a, as_stream(stream)), "mx_dequantize");
+}
+
+static mx_status check_swiglu_common(const char* fn, int64_t rows, int64_t hidden, mx_scale_mode mode,
+                                     uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col) {
+  MX_REQUIRE(mode == MX_RCEIL || mode == MX_FLOOR, MX_ERR_ARG, "%s: bad scale mode", fn);
+  MX_REQUIRE(rows >= 0 && hidden >= 0 && rows % 32 == 0 && hidden % 32 == 0, MX_ERR_SHAPE,
+             "%s: rows and hidden must be non-negative multiples of 32", fn);
+  MX_REQUIRE((rows + 127) / 128 <= 65535, MX_ERR_SHAPE, "%s: too many rows for one launch", fn);
+  if (rows == 0 || hidden == 0) return MX_OK;
+  MX_REQUIRE(q_row && s_row && q_col && s_col, MX_ERR_NULL, "%s: NULL output", fn);
+  MX_REQUIRE(al16(q_row) && al16(q_col), MX_ERR_ALIGN, "%s: code outputs must be 16-byte aligned", fn);
+  return MX_OK;
+}
+
+mx_status mx_swiglu_quant_fwd(const void* a, const void* b, int64_t ld_ab, int64_t rows, int64_t hidden,
+                              mx_scale_mode mode, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                              uint8_t* s_col, void* h_out, void* stream) {
+  mx_status st = check_swiglu_common("mx_swiglu_quant_fwd", rows, hidden, mode, q_row, s_row, q_col, s_col);
+  if (st != MX_OK || rows == 0 || hidden == 0) return st;
+  MX_REQUIRE(a && b, MX_ERR_NULL, "mx_swiglu_quant_fwd: a/b NULL");
+  MX_REQUIRE(al16(a) && al16(b) && ld_ab >= hidden && ld_ab % 8 == 0, MX_ERR_ALIGN,
+             "mx_swiglu_quant_fwd: a/b must be 16-byte aligned, ld_ab >= hidden and a multiple of 8");
+  MX_REQUIRE(!h_out || al16(h_out), MX_ERR_ALIGN, "mx_swiglu_quant_fwd: h_out must be 16-byte aligned");
+  MX_DEVICE();
+  mxk::SwigluFwdArgs k{static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), ld_ab, rows, hidden,
+                       mode == MX_RCEIL, q_row, s_row, q_col, s_col, static_cast<uint16_t*>(h_out)};
+  return launched(mxk::launch_swiglu_fwd(k, as_stream(stream)), "mx_swiglu_quant_fwd");
+}
+
+mx_status mx_swiglu_quant_bwd(const void* dh, int64_t ld_dh, const void* a, const void* b, int64_t ld_ab,
+                              int64_t rows, int64_t hidden, mx_scale_mode mode, uint8_t* q_row,
+                              uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, void* dab_out, void* stream) {
+  mx_status st = check_swiglu_common("mx_swiglu_quant_bwd", rows, hidden, mode, q_row, s_row, q_col, s_col);
+  if (st != MX_OK || rows == 0 || hidden == 0) return st;
+  MX_REQUIRE(dh && a && b, MX_ERR_NULL, "mx_swiglu_quant_bwd: dh/a/b NULL");
+  MX_REQUIRE(al16(dh) && al16(a) && al16(b) && ld_ab >= hidden && ld_ab % 8 == 0 && ld_dh >= hidden &&
+                 ld_dh % 8 == 0,
+             MX_ERR_ALIGN, "mx_swiglu_quant_bwd: inputs must be 16-byte aligned with ld >= hidden, ld % 8 == 0");
+  MX_REQUIRE(!dab_out || al16(dab_out), MX_ERR_ALIGN, "mx_swiglu_quant_bwd: dab_out must be 16-byte aligned");
+  MX_DEVICE();
+  mxk::SwigluBwdArgs k{static_cast<const uint16_t*>(dh), static_cast<const uint16_t*>(a),
+                       static_cast<const uint16_t*>(b), ld_dh, ld_ab, rows, hidden, mode == MX_RCEIL,
+                       q_row, s_row, q_col, s_col, static_cast<uint16_t*>(dab_out)};
+  return launched(mxk::launch_swiglu_bwd(k, as_stream(stream)), "mx_swiglu_quant_bwd");
+}
+
+static mx_status check_mx_operand(const char* fn, const char* name, const uint8_t* q, const uint8_t* s) {
+  MX_REQUIRE(q && s, MX_ERR_NULL, "%s: %s codes/scales NULL", fn, name);
+  MX_REQUIRE(al16(q), MX_ERR_ALIGN, "%s: %s codes must be 16-byte aligned", fn, name);
+  MX_REQUIRE((reinterpret_cast<uintptr_t>(s) & 3u) == 0, MX_ERR_ALIGN, "%s: %s scales must be 4-byte aligned", fn, name);
+  return MX_OK;
+}
+
+#define MX_CHECK(expr)              \
+  do {                              \
+    mx_status st_ = (expr);         \
+    if (st_ != MX_OK) return st_;   \
+  } while (0)
+
+mx_status mx_scaled_mm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
+                       int64_t M, int64_t N, int64_t K, mx_dtype out_dtype, void* out, int64_t ld_out,
+                       void* stream) {
+  const char* fn = "mx_scaled_mm";
+  MX_REQUIRE(out_dtype == MX_BF16 || out_dtype == MX_F32, MX_ERR_ARG, "%s: bad dtype", fn);
+  MX_REQUIRE(M >= 0 && N >= 0 && K > 0 && K % 128 == 0, MX_ERR_SHAPE, "%s: K (%lld) must be a positive multiple of 128", fn, (long long)K);
+  MX_REQUIRE((M + 255) / 256 <= 65535 && (N + 255) / 256 <= 65535, MX_ERR_SHAPE, "%s: M or N too large", fn);
+  if (M == 0 || N == 0) return MX_OK;
+  MX_CHECK(check_mx_operand(fn, "A", qa, sa));
+  MX_CHECK(check_mx_operand(fn, "B", qb, sb));
+  const int esz = out_dtype == MX_F32 ? 4 : 2;
+  MX_REQUIRE(out, MX_ERR_NULL, "%s: out NULL", fn);
+  MX_REQUIRE(al16(out) && ld_out >= N && (ld_out * esz) % 16 == 0, MX_ERR_ALIGN,
+             "%s: out must be 16-byte aligned and ld_out >= N with 16-byte rows", fn);
+  MX_DEVICE();
+  mxk::GemmArgs a{};
+  a.qa = qa; a.sa = sa; a.qb = qb; a.sb = sb;
+  a.M = M; a.N = N; a.K = K;
+  a.lda = K; a.ldb = K; a.ldsa = K / 32; a.ldsb = K / 32;
+  a.out = out; a.ldo = ld_out; a.out_f32 = out_dtype == MX_F32;
+  return launched(mxk::launch_gemm_dense(a, as_stream(stream)), fn);
+}
+
+static mx_status grouped_2d3d(const char* fn, const uint8_t* qa, const uint8_t* sa, const uint8_t* qw,
+                              const uint8_t* sw, const int32_t* offs, int32_t E, int64_t Tcap, int64_t N,
+                              int64_t K, mx_dtype out_dtype, void* out, int32_t* dev_err, void* stream) {
+  MX_REQUIRE(out_dtype == MX_BF16 || out_dtype == MX_F32, MX_ERR_ARG, "%s: bad dtype", fn);
+  MX_REQUIRE(E >= 1 && E <= 1024, MX_ERR_SHAPE, "%s: E (%d) must be in [1, 1024]", fn, E);
+  MX_REQUIRE(Tcap >= 0 && Tcap % 128 == 0, MX_ERR_SHAPE, "%s: Tcap must be a multiple of 128", fn);
+  MX_REQUIRE(N > 0 && N % 16 == 0, MX_ERR_SHAPE, "%s: N must be a positive multiple of 16", fn);
+  MX_REQUIRE(K > 0 && K % 128 == 0, MX_ERR_SHAPE, "%s: K must be a positive multiple of 128", fn);
+  MX_REQUIRE(Tcap / 256 + E <= 65535 && (N + 255) / 256 <= 65535, MX_ERR_SHAPE, "%s: too large", fn);
+  if (Tcap == 0) return MX_OK;
+  MX_CHECK(check_mx_operand(fn, "A", qa, sa));
+  MX_CHECK(check_mx_operand(fn, "W", qw, sw));
+  MX_REQUIRE(offs && out, MX_ERR_NULL, "%s: offs/out NULL", fn);
+  MX_REQUIRE(al16(out), MX_ERR_ALIGN, "%s: out must be 16-byte aligned", fn);
+  MX_DEVICE();
+  mxk::GemmArgs a{};
+  a.qa = qa; a.sa = sa; a.qb = qw; a.sb = sw;
+  a.M = Tcap; a.N = N; a.K = K;
+  a.lda = K; a.ldb = K; a.ldsa = K / 32; a.ldsb = K / 32;
+  a.b_group_stride = N * K; a.sb_group_stride = N * (K / 32);
+  a.out = out; a.ldo = N; a.out_f32 = out_dtype == MX_F32;
+  a.offs = offs; a.E = E; a.dev_err = dev_err;
+  return launched(mxk::launch_gemm_grouped(a, as_stream(stream)), fn);
+}
+
+mx_status mx_scaled_grouped_mm_fwd(const uint8_t* qa, const uint8_t* sa, const uint8_t* qw, const uint8_t* sw,
+                                   const int32_t* offs, int32_t E, int64_t Tcap, int64_t N, int64_t K,
+                                   mx_dtype out_dtype, void* out, int32_t* dev_err, void* stream) {
+  return grouped_2d3d("mx_scaled_grouped_mm_fwd", qa, sa, qw, sw, offs, E, Tcap, N, K, out_dtype, out,
+                      dev_err, stream);
+}
+
+mx_status mx_scaled_grouped_mm_dgrad(const uint8_t* qa, const uint8_t* sa, const uint8_t* qw,
+                                     const uint8_t* sw, const int32_t* offs, int32_t E, int64_t Tcap,
+                                     int64_t N, int64_t K, mx_dtype out_dtype, void* out, int32_t* dev_err,
+                                     void* stream) {
+  return grouped_2d3d("mx_scaled_grouped_mm_dgrad", qa, sa, qw, sw, offs, E, Tcap, N, K, out_dtype, out,
+                      dev_err, stream);
+}
+
+mx_status mx_scaled_grouped_mm_wgrad(const uint8_t* qg, const uint8_t* sg, const uint8_t* qx,
+                                     const uint8_t* sx, const int32_t* offs, int32_t E, int64_t Tcap,
+                                     int64_t N, int64_t K, mx_dtype out_dtype, void* out, int32_t* dev_err,
+                                     void* stream) {
+  const char* fn = "mx_scaled_grouped_mm_wgrad";
+  MX_REQUIRE(out_dtype == MX_BF16 || out_dtype == MX_F32, MX_ERR_ARG, "%s: bad dtype", fn);
+  MX_REQUIRE(E >= 1 && E <= 1024 && E <= 65535, MX_ERR_SHAPE, "%s: E must be in [1, 1024]", fn);
+  MX_REQUIRE(Tcap >= 0 && Tcap % 128 == 0, MX_ERR_SHAPE, "%s: Tcap must be a multiple of 128", fn);
+  MX_REQUIRE(N > 0 && N % 16 == 0 && K > 0 && K % 16 == 0, MX_ERR_SHAPE, "%s: N and K must be positive multiples of 16", fn);
+  MX_REQUIRE((N + 255) / 256 <= 65535 && (K + 255) / 256 <= 65535, MX_ERR_SHAPE, "%s: too large", fn);
+  MX_CHECK(check_mx_operand(fn, "G", qg, sg));
+  MX_CHECK(check_mx_operand(fn, "X", qx, sx));
+  MX_REQUIRE(offs && out, MX_ERR_NULL, "%s: offs/out NULL", fn);
+  MX_REQUIRE(al16(out), MX_ERR_ALIGN, "%s: out must be 16-byte aligned", fn);
+  MX_DEVICE();
+  mxk::GemmArgs a{};
+  a.qa = qg; a.sa = sg; a.qb = qx; a.sb = sx;
+  a.M = Tcap; a.N = N; a.K = K;
+  a.lda = Tcap; a.ldb = Tcap; a.ldsa = Tcap / 32; a.ldsb = Tcap / 32;
+  a.out_group_stride = N * K;
+  a.out = out; a.ldo = K; a.out_f32 = out_dtype == MX_F32;
+  a.offs = offs; a.E = E; a.dev_err = dev_err;
+  return launched(mxk::launch_gemm_wgrad(a, as_stream(stream)), fn);
+}
+
+mx_status mx_grouped_mm_wgrad_hp(const void* g, const void* x, const int32_t* offs, int32_t E, int64_t Tcap,
+                                 int64_t N, int64_t K, void* out, int32_t* dev_err, void* stream) {
+  const char* fn = "mx_grouped_mm_wgrad_hp";
+  MX_REQUIRE(E >= 1 && E <= 1024, MX_ERR_SHAPE, "%s: E must be in [1, 1024]", fn);
+  MX_REQUIRE(Tcap >= 0 && Tcap % 128 == 0, MX_ERR_SHAPE, "%s: Tcap must be a multiple of 128", fn);
+  MX_REQUIRE(N > 0 && N % 16 == 0 && K > 0 && K % 16 == 0, MX_ERR_SHAPE, "%s: N and K must be positive multiples of 16", fn);
+  MX_REQUIRE((N + 127) / 128 <= 65535 && (K + 127) / 128 <= 65535, MX_ERR_SHAPE, "%s: too large", fn);
+  MX_REQUIRE(g && x && offs && out, MX_ERR_NULL, "%s: NULL pointer", fn);
+  MX_REQUIRE(al16(g) && al16(x) && al16(out), MX_ERR_ALIGN, "%s: g/x/out must be 16-byte aligned", fn);
+  MX_DEVICE();
+  mxk::HpWgradArgs a{static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(x), offs, E, Tcap, N, K,
+                     static_cast<uint16_t*>(out), dev_err};
+  return launched(mxk::launch_hp_wgrad(a, as_stream(stream)), fn);
+}
+
+mx_status mx_pad_groups(const void* x, const int32_t* group_sizes, int32_t E, int64_t T, int64_t row_bytes,
+                        int32_t pad_multiple, int64_t Tcap, void* x_pad, int32_t* offs_pad, int32_t* src_row,
+                        int32_t* dev_err, void* stream) {
+  const char* fn = "mx_pad_groups";
+  MX_REQUIRE(E >= 1 && E <= 1024, MX_ERR_SHAPE, "%s: E must be in [1, 1024]", fn);
+  MX_REQUIRE(T >= 0 && Tcap >= 0 && T < (1ll << 31) && Tcap < (1ll << 31), MX_ERR_SHAPE, "%s: T/Tcap out of range", fn);
+  MX_REQUIRE(row_bytes > 0 && row_bytes % 16 == 0, MX_ERR_SHAPE, "%s: row_bytes must be a positive multiple of 16", fn);
+  MX_REQUIRE(pad_multiple > 0 && pad_multiple % 32 == 0, MX_ERR_SHAPE, "%s: pad_multiple must be a positive multiple of 32", fn);
+  MX_REQUIRE(group_sizes && offs_pad && (Tcap == 0 || (x_pad && src_row)) && (T == 0 || x), MX_ERR_NULL,
+             "%s: NULL pointer", fn);
+  MX_REQUIRE((T == 0 || al16(x)) && (Tcap == 0 || al16(x_pad)), MX_ERR_ALIGN, "%s: x/x_pad must be 16-byte aligned", fn);
+  MX_DEVICE();
+  mxk::PadArgs a{static_cast<const uint8_t*>(x), group_sizes, E, T, row_bytes, Tcap, pad_multiple,
+                 static_cast<uint8_t*>(x_pad), offs_pad, src_row, dev_err};
+  return launched(mxk::launch_pad(a, as_stream(stream)), fn);
+}
+
+mx_status mx_unpad_groups(const void* y_pad, const int32_t* src_row, int64_t Tcap, int64_t T, int64_t row_bytes,
+                          void* y, void* stream) {
+  const char* fn = "mx_unpad_groups";
+  MX_REQUIRE(T >= 0 && Tcap >= 0 && Tcap < (1ll << 31), MX_ERR_SHAPE, "%s: T/Tcap out of range", fn);
+  MX_REQUIRE(row_bytes > 0 && row_bytes % 16 == 0, MX_ERR_SHAPE, "%s: row_bytes must be a positive multiple of 16", fn);
+  if (Tcap == 0 || T == 0) return MX_OK;
+  MX_REQUIRE(y_pad && src_row && y, MX_ERR_NULL, "%s: NULL pointer", fn);
+  MX_REQUIRE(al16(y_pad) && al16(y), MX_ERR_ALIGN, "%s: y/y_pad must be 16-byte aligned", fn);
+  MX_DEVICE();
+  mxk::UnpadArgs a{static_cast<const uint8_t*>(y_pad), src_row, Tcap, T, row_bytes, static_cast<uint8_t*>(y)};
+  return launched(mxk::launch_unpad(a, as_stream(stream)), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Kernel argument blocks and launch entry points of libmxfp8.so (internal to
+// the library; the public interface is include/mxfp8.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxk {
+
+struct QuantArgs {
+  const uint16_t* x;
+  int64_t rows, cols, ld;
+  bool rceil;
+  uint8_t *q_row, *s_row, *q_col, *s_col;
+};
+
+struct SwigluFwdArgs {
+  const uint16_t *a, *b;
+  int64_t ld_ab, rows, hidden;
+  bool rceil;
+  uint8_t *q_row, *s_row, *q_col, *s_col;
+  uint16_t* h_out;
+};
+
+struct SwigluBwdArgs {
+  const uint16_t *dh, *a, *b;
+  int64_t ld_dh, ld_ab, rows, hidden;
+  bool rceil;
+  uint8_t *q_row, *s_row, *q_col, *s_col;
+  uint16_t* dab_out;
+};
+
+struct DequantArgs {
+  const uint8_t *q, *s;
+  int64_t rows, cols;
+  bool out_f32;
+  void* out;
+};
+
+// C[m, n] = sum_k A[m, k] B[n, k] over MX operands (see mx_gemm.hip).
+struct GemmArgs {
+  const uint8_t *qa, *sa, *qb, *sb;
+  int64_t M, N, K;          // dense: sizes; grouped: M = Tcap
+  int64_t lda, ldb;         // code bytes per operand row
+  int64_t ldsa, ldsb;       // scale bytes per operand row
+  int64_t b_group_stride;   // grouped fwd/dgrad: bytes between experts' B
+  int64_t sb_group_stride;  // and between their scales
+  int64_t out_group_stride; // wgrad: elements between experts' outputs
+  void* out;
+  int64_t ldo;              // output elements per row
+  bool out_f32;
+  const int32_t* offs;
+  int32_t E;
+  int32_t* dev_err;
+};
+
+struct PadArgs {
+  const uint8_t* x;
+  const int32_t* sizes;
+  int32_t E;
+  int64_t T, row_bytes, Tcap;
+  int32_t multiple;
+  uint8_t* x_pad;
+  int32_t *offs_pad, *src_row, *dev_err;
+};
+
+struct UnpadArgs {
+  const uint8_t* y_pad;
+  const int32_t* src_row;
+  int64_t Tcap, T, row_bytes;
+  uint8_t* y;
+};
+
+struct HpWgradArgs {
+  const uint16_t *g, *x;
+  const int32_t* offs;
+  int32_t E;
+  int64_t Tcap, N, K;
+  uint16_t* out;
+  int32_t* dev_err;
+};
+
+// Launchers: return hipSuccess or the launch error. Shapes are validated by
+// the caller (mx_abi.cpp).
+hipError_t launch_quant(const QuantArgs& a, int64_t batch, hipStream_t s);
+hipError_t launch_swiglu_fwd(const SwigluFwdArgs& a, hipStream_t s);
+hipError_t launch_swiglu_bwd(const SwigluBwdArgs& a, hipStream_t s);
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
+hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_wgrad(const GemmArgs& a, hipStream_t s);
+hipError_t launch_pad(const PadArgs& a, hipStream_t s);
+hipError_t launch_unpad(const UnpadArgs& a, hipStream_t s);
+hipError_t launch_hp_wgrad(const HpWgradArgs& a, hipStream_t s);
+
+}  // namespace mxk

@@ -1,0 +1,332 @@
+// Bandwidth-bound kernels of the MXFP8 hot path on gfx950:
+//   k_quant_tile      MX block quantization, row-wise and/or column-wise
+//   k_swiglu_fwd      fused SwiGLU + dual MX quantization (forward)
+//   k_swiglu_bwd      fused SwiGLU backward + dual MX quantization
+//   k_dequant         E4M3 x E8M0 -> float32 / bf16
+//
+// All four share one tile scheme. A 256-thread workgroup owns a 128 x 128
+// tile of bf16 values. Thread t holds 8 chunks of 8 consecutive values (one
+// 16-byte load each): chunk j sits at tile row (t >> 4) + 16 j, columns
+// 8 (t & 15) .. 8 (t & 15) + 7, so the 4 lanes of a quad hold one 32-value
+// row block and the block maximum is two DPP quad permutes away.
+// Row-wise quantization is done straight from registers. For column-wise
+// quantization the tile is written to LDS (dword = two adjacent columns) and
+// each thread reads one 32-row block of a column pair back: 64 lanes read 64
+// consecutive dwords per row, which is free of bank conflicts, and each lane
+// then writes 32 contiguous code bytes per column.
+//
+// The fused SwiGLU kernels produce their tile in registers from the inputs
+// (h = silu(a) * b, or dA / dB), round it to bf16 and run the same two
+// quantizations, so the bf16 activation never goes to memory unless asked.
+
+#include "mx_device.h"
+#include "mx_kernels.h"
+
+#include <algorithm>
+
+namespace mxk {
+
+constexpr int kTR = 128;                 // tile rows
+constexpr int kTC = 128;                 // tile columns
+constexpr int kTileThreads = 256;
+constexpr int kTileChunks = kTR * kTC / 8 / kTileThreads;   // 8 per thread
+
+struct TileOut {
+  uint8_t* q;      // codes
+  uint8_t* s;      // scales
+  int64_t ld;      // codes per output row (scale row = ld / 32 bytes)
+};
+
+// Row-wise quantization of the thread's 8 chunks. The tile's (0,0) sits at
+// row r0, column c0 of the output. All lanes must reach this function.
+__device__ __forceinline__ void tile_rowq(const uint4 (&v)[kTileChunks], int rows_valid,
+                                          int cols_valid, bool rceil, TileOut o, int64_t r0,
+                                          int64_t c0) {
+  const int t = threadIdx.x;
+  const int cc = t & 15;
+  const bool colok = cc * 8 < cols_valid;
+#pragma unroll
+  for (int j = 0; j < kTileChunks; ++j) {
+    const int row = (t >> 4) + 16 * j;
+    const uint32_t sb = scale_byte(quad_max(absmax8_bits(v[j])), rceil);
+    const uint2 codes = e4m3_chunk(v[j], inv_scale(sb), sb == 0xFFu);
+    if (row < rows_valid && colok) {
+      const int64_t orow = r0 + row;
+      const int64_t ocol = c0 + cc * 8;
+      *reinterpret_cast<uint2*>(o.q + orow * o.ld + ocol) = codes;
+      if ((cc & 3) == 0) o.s[orow * (o.ld / kBlock) + ocol / kBlock] = (uint8_t)sb;
+    }
+  }
+}
+
+// Stage the thread's chunks in LDS (row-major, 64 dwords per tile row).
+__device__ __forceinline__ void tile_to_lds(const uint4 (&v)[kTileChunks], uint4* lds) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kTileChunks; ++j) lds[((t >> 4) + 16 * j) * (kTC / 8) + (t & 15)] = v[j];
+}
+
+// Column-wise quantization from the LDS tile: thread t takes columns
+// 2p, 2p+1 (p = t & 63) and rows 32 b .. 32 b + 31 (b = t >> 6) of the tile,
+// i.e. one output block in each of two output rows. Output row = tile
+// column c0 + col, output column = tile row r0 + row.
+__device__ __forceinline__ void tile_colq(const uint4* lds4, int rows_valid, int cols_valid,
+                                          bool rceil, TileOut o, int64_t r0, int64_t c0) {
+  const uint32_t* lds = reinterpret_cast<const uint32_t*>(lds4);
+  const int t = threadIdx.x;
+  const int p = t & 63;
+  const int b = t >> 6;
+  if (2 * p >= cols_valid || 32 * b >= rows_valid) return;
+  uint32_t w[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i] = lds[(32 * b + i) * (kTC / 2) + p];
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+  us2 m = __builtin_bit_cast(us2, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+  for (int i = 1; i < 32; ++i)
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w[i] & 0x7FFF7FFFu));
+  const uint32_t sb0 = scale_byte(m.x, rceil);
+  const uint32_t sb1 = scale_byte(m.y, rceil);
+  const float mul0 = inv_scale(sb0), mul1 = inv_scale(sb1);
+  uint32_t c0w[8], c1w[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uint32_t a0 = 0, a1 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = w[4 * k + i];
+      a0 |= e4m3_code(bf16_lo(x) * mul0) << (8 * i);
+      a1 |= e4m3_code(bf16_hi(x) * mul1) << (8 * i);
+    }
+    if (sb0 == 0xFFu) {
+      a0 = 0x7F7F7F7Fu;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a0 |= ((w[4 * k + i] >> 15) & 1u) << (8 * i + 7);
+    }
+    if (sb1 == 0xFFu) {
+      a1 = 0x7F7F7F7Fu;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a1 |= ((w[4 * k + i] >> 31) & 1u) << (8 * i + 7);
+    }
+    c0w[k] = a0;
+    c1w[k] = a1;
+  }
+  const int64_t orow0 = c0 + 2 * p;
+  const int64_t ocol = r0 + 32 * b;
+  uint4* d0 = reinterpret_cast<uint4*>(o.q + orow0 * o.ld + ocol);
+  uint4* d1 = reinterpret_cast<uint4*>(o.q + (orow0 + 1) * o.ld + ocol);
+  d0[0] = make_uint4(c0w[0], c0w[1], c0w[2], c0w[3]);
+  d0[1] = make_uint4(c0w[4], c0w[5], c0w[6], c0w[7]);
+  d1[0] = make_uint4(c1w[0], c1w[1], c1w[2], c1w[3]);
+  d1[1] = make_uint4(c1w[4], c1w[5], c1w[6], c1w[7]);
+  o.s[orow0 * (o.ld / kBlock) + ocol / kBlock] = (uint8_t)sb0;
+  o.s[(orow0 + 1) * (o.ld / kBlock) + ocol / kBlock] = (uint8_t)sb1;
+}
+
+// Loads the thread's chunks of a bf16 tile whose (0,0) is `base` with row
+// stride ld elements; chunks outside the valid region read as zero.
+__device__ __forceinline__ void tile_load(uint4 (&v)[kTileChunks], const uint16_t* base,
+                                          int64_t ld, int rows_valid, int cols_valid) {
+  const int t = threadIdx.x;
+  const int cc = t & 15;
+#pragma unroll
+  for (int j = 0; j < kTileChunks; ++j) {
+    const int row = (t >> 4) + 16 * j;
+    v[j] = (row < rows_valid && cc * 8 < cols_valid)
+               ? *reinterpret_cast<const uint4*>(base + row * ld + cc * 8)
+               : make_uint4(0, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void tile_store_bf16(const uint4 (&v)[kTileChunks], uint16_t* base,
+                                                int64_t ld, int rows_valid, int cols_valid) {
+  const int t = threadIdx.x;
+  const int cc = t & 15;
+#pragma unroll
+  for (int j = 0; j < kTileChunks; ++j) {
+    const int row = (t >> 4) + 16 * j;
+    if (row < rows_valid && cc * 8 < cols_valid)
+      *reinterpret_cast<uint4*>(base + row * ld + cc * 8) = v[j];
+  }
+}
+
+// ---------------------------------------------------------------- quantize
+
+__global__ __launch_bounds__(kTileThreads) void k_quant_tile(QuantArgs a) {
+  __shared__ uint4 lds[kTR * kTC / 8];
+  const int64_t bz = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.y * kTR;
+  const int64_t c0 = (int64_t)blockIdx.x * kTC;
+  const int rows_valid = (int)min<int64_t>(kTR, a.rows - r0);
+  const int cols_valid = (int)min<int64_t>(kTC, a.cols - c0);
+  uint4 v[kTileChunks];
+  tile_load(v, a.x + (bz * a.rows + r0) * a.ld + c0, a.ld, rows_valid, cols_valid);
+  if (a.q_row) {
+    TileOut o{a.q_row + bz * a.rows * a.cols, a.s_row + bz * a.rows * (a.cols / kBlock), a.cols};
+    tile_rowq(v, rows_valid, cols_valid, a.rceil, o, r0, c0);
+  }
+  if (a.q_col) {
+    tile_to_lds(v, lds);
+    __syncthreads();
+    TileOut o{a.q_col + bz * a.rows * a.cols, a.s_col + bz * a.cols * (a.rows / kBlock), a.rows};
+    tile_colq(lds, rows_valid, cols_valid, a.rceil, o, r0, c0);
+  }
+}
+
+// ---------------------------------------------------------------- SwiGLU
+
+// silu(a) * b in float32 with the accurate expf and an IEEE division.
+__device__ __forceinline__ float swiglu_f32(float a, float b) {
+  const float s = 1.0f / (1.0f + expf(-a));
+  return (a * s) * b;
+}
+
+__device__ __forceinline__ uint32_t swiglu_pair(uint32_t wa, uint32_t wb) {
+  return pack_bf16x2(swiglu_f32(bf16_lo(wa), bf16_lo(wb)), swiglu_f32(bf16_hi(wa), bf16_hi(wb)));
+}
+
+__global__ __launch_bounds__(kTileThreads) void k_swiglu_fwd(SwigluFwdArgs a) {
+  __shared__ uint4 lds[kTR * kTC / 8];
+  const int64_t r0 = (int64_t)blockIdx.y * kTR;
+  const int64_t c0 = (int64_t)blockIdx.x * kTC;
+  const int rows_valid = (int)min<int64_t>(kTR, a.rows - r0);
+  const int cols_valid = (int)min<int64_t>(kTC, a.hidden - c0);
+  uint4 v[kTileChunks], w[kTileChunks];
+  tile_load(v, a.a + r0 * a.ld_ab + c0, a.ld_ab, rows_valid, cols_valid);
+  tile_load(w, a.b + r0 * a.ld_ab + c0, a.ld_ab, rows_valid, cols_valid);
+#pragma unroll
+  for (int j = 0; j < kTileChunks; ++j)
+    v[j] = make_uint4(swiglu_pair(v[j].x, w[j].x), swiglu_pair(v[j].y, w[j].y),
+                      swiglu_pair(v[j].z, w[j].z), swiglu_pair(v[j].w, w[j].w));
+  if (a.h_out) tile_store_bf16(v, a.h_out + r0 * a.hidden + c0, a.hidden, rows_valid, cols_valid);
+  tile_rowq(v, rows_valid, cols_valid, a.rceil, TileOut{a.q_row, a.s_row, a.hidden}, r0, c0);
+  tile_to_lds(v, lds);
+  __syncthreads();
+  tile_colq(lds, rows_valid, cols_valid, a.rceil, TileOut{a.q_col, a.s_col, a.rows}, r0, c0);
+}
+
+// dA = dh*b*s*(1 + a*(1-s)), dB = dh*a*s with s = sigmoid(a), float32.
+__device__ __forceinline__ void swiglu_grad_f32(float dh, float a, float b, float& da,
+                                                float& db) {
+  const float s = 1.0f / (1.0f + expf(-a));
+  da = (dh * b) * (s * (1.0f + a * (1.0f - s)));
+  db = dh * (a * s);
+}
+
+__device__ __forceinline__ void swiglu_grad_pair(uint32_t wdh, uint32_t wa, uint32_t wb,
+                                                 uint32_t& da2, uint32_t& db2) {
+  float da0, db0, da1, db1;
+  swiglu_grad_f32(bf16_lo(wdh), bf16_lo(wa), bf16_lo(wb), da0, db0);
+  swiglu_grad_f32(bf16_hi(wdh), bf16_hi(wa), bf16_hi(wb), da1, db1);
+  da2 = pack_bf16x2(da0, da1);
+  db2 = pack_bf16x2(db0, db1);
+}
+
+__global__ __launch_bounds__(kTileThreads) void k_swiglu_bwd(SwigluBwdArgs a) {
+  __shared__ uint4 lds[kTR * kTC / 8];
+  const int64_t r0 = (int64_t)blockIdx.y * kTR;
+  const int64_t c0 = (int64_t)blockIdx.x * kTC;
+  const int rows_valid = (int)min<int64_t>(kTR, a.rows - r0);
+  const int cols_valid = (int)min<int64_t>(kTC, a.hidden - c0);
+  const int64_t H2 = 2 * a.hidden;
+  uint4 da[kTileChunks], db[kTileChunks];
+  {
+    uint4 vdh[kTileChunks], va[kTileChunks];
+    tile_load(vdh, a.dh + r0 * a.ld_dh + c0, a.ld_dh, rows_valid, cols_valid);
+    tile_load(va, a.a + r0 * a.ld_ab + c0, a.ld_ab, rows_valid, cols_valid);
+    tile_load(db, a.b + r0 * a.ld_ab + c0, a.ld_ab, rows_valid, cols_valid);
+#pragma unroll
+    for (int j = 0; j < kTileChunks; ++j) {
+      uint4 x, y;
+      swiglu_grad_pair(vdh[j].x, va[j].x, db[j].x, x.x, y.x);
+      swiglu_grad_pair(vdh[j].y, va[j].y, db[j].y, x.y, y.y);
+      swiglu_grad_pair(vdh[j].z, va[j].z, db[j].z, x.z, y.z);
+      swiglu_grad_pair(vdh[j].w, va[j].w, db[j].w, x.w, y.w);
+      da[j] = x;
+      db[j] = y;
+    }
+  }
+  if (a.dab_out) {
+    tile_store_bf16(da, a.dab_out + r0 * H2 + c0, H2, rows_valid, cols_valid);
+    tile_store_bf16(db, a.dab_out + r0 * H2 + a.hidden + c0, H2, rows_valid, cols_valid);
+  }
+  const TileOut orow{a.q_row, a.s_row, H2};
+  tile_rowq(da, rows_valid, cols_valid, a.rceil, orow, r0, c0);
+  tile_rowq(db, rows_valid, cols_valid, a.rceil, orow, r0, a.hidden + c0);
+  const TileOut ocol{a.q_col, a.s_col, a.rows};
+  tile_to_lds(da, lds);
+  __syncthreads();
+  tile_colq(lds, rows_valid, cols_valid, a.rceil, ocol, r0, c0);
+  __syncthreads();
+  tile_to_lds(db, lds);
+  __syncthreads();
+  tile_colq(lds, rows_valid, cols_valid, a.rceil, ocol, r0, a.hidden + c0);
+}
+
+// ---------------------------------------------------------------- dequantize
+
+// Thread per 16 codes (a half block): one 16-byte code load, one scale byte.
+__global__ __launch_bounds__(256) void k_dequant(DequantArgs a) {
+  const int64_t n16 = a.rows * a.cols / 16;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+    const uint4 c = *reinterpret_cast<const uint4*>(a.q + 16 * i);
+    const uint32_t sb = a.s[i >> 1];
+    uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    float f[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float v = e4m3_value((w[k >> 2] >> (8 * (k & 3))) & 0xFFu);
+      // v has at most 4 significant bits and |v| >= 2^-9, so v * 2^(sb-127)
+      // is exact in float32 down to 2^-136 (a float32 subnormal); only
+      // E = 127 with |v| > 1 overflows, to infinity
+      f[k] = sb == 0xFFu ? __uint_as_float(0x7FC00000u) : ldexpf(v, (int)sb - 127);
+    }
+    if (a.out_f32) {
+      float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + 16 * i);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] = make_float4(f[4 * k], f[4 * k + 1], f[4 * k + 2], f[4 * k + 3]);
+    } else {
+      uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + 16 * i);
+      o[0] = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                        pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+      o[1] = make_uint4(pack_bf16x2(f[8], f[9]), pack_bf16x2(f[10], f[11]),
+                        pack_bf16x2(f[12], f[13]), pack_bf16x2(f[14], f[15]));
+    }
+  }
+}
+
+}  // namespace mxk
+
+// ---------------------------------------------------------------- launch
+
+namespace mxk {
+
+hipError_t launch_quant(const QuantArgs& a, int64_t batch, hipStream_t s) {
+  dim3 grid((unsigned)((a.cols + kTC - 1) / kTC), (unsigned)((a.rows + kTR - 1) / kTR),
+            (unsigned)batch);
+  hipLaunchKernelGGL(k_quant_tile, grid, dim3(kTileThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_fwd(const SwigluFwdArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)((a.hidden + kTC - 1) / kTC), (unsigned)((a.rows + kTR - 1) / kTR));
+  hipLaunchKernelGGL(k_swiglu_fwd, grid, dim3(kTileThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const SwigluBwdArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)((a.hidden + kTC - 1) / kTC), (unsigned)((a.rows + kTR - 1) / kTR));
+  hipLaunchKernelGGL(k_swiglu_bwd, grid, dim3(kTileThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {
+  const int64_t n16 = a.rows * a.cols / 16;
+  if (n16 == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n16 + 255) / 256, 256 * 64);
+  hipLaunchKernelGGL(k_dequant, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mxk

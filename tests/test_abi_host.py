@@ -1,0 +1,68 @@
+"""Host-side checks of libmxfp8.so without a GPU: the library loads, exports
+every entry point that include/mxfp8.h declares (and the binding binds all of
+them), and argument errors are reported before any device work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantize_grouped_gemm_amd import mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp8.h")
+
+
+def _lib():
+    if not os.path.exists(mx.LIB_PATH):
+        from quantize_grouped_gemm_amd import build
+        build.build()
+    return mx.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported_and_bound():
+    L = _lib()
+    names = _declared()
+    assert len(names) == 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(mx.EXPORTS) == names
+    assert L.mx_abi_version() == 1
+
+
+def test_argument_errors_are_reported_without_device_work():
+    L = _lib()
+    p = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    # cols not a multiple of 32
+    st = L.mx_quantize(p, 1, 64, 48, 48, 0, 1, p, p, None, None, None)
+    assert st == 2 and b"multiple of 32" in L.mx_last_error()
+    # bad scale mode / direction bits
+    assert L.mx_quantize(p, 1, 64, 64, 64, 7, 1, p, p, None, None, None) == 4
+    assert L.mx_quantize(p, 1, 64, 64, 64, 0, 8, p, p, None, None, None) == 4
+    # misaligned pointer
+    assert L.mx_quantize(ctypes.c_void_p(18), 1, 64, 64, 64, 0, 1, p, p, None, None, None) == 3
+    # K not a multiple of 128
+    assert L.mx_scaled_mm(p, p, p, p, 32, 32, 96, 0, p, 32, None) == 2
+    # grouped: Tcap not a multiple of 128, bad E
+    assert L.mx_scaled_grouped_mm_fwd(p, p, p, p, p, 4, 100, 64, 128, 0, p, None, None) == 2
+    assert L.mx_scaled_grouped_mm_wgrad(p, p, p, p, p, 0, 128, 64, 64, 1, p, None, None) == 2
+    assert L.mx_pad_groups(p, p, 2, 10, 24, 128, 256, p, p, p, None, None) == 2
+    assert L.mx_unpad_groups(p, p, 128, 10, 32, None, None) == 1
+
+
+def test_valid_call_without_gpu_fails_loudly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the device path is covered by the gpu tests")
+    L = _lib()
+    p = ctypes.c_void_p(16)
+    st = L.mx_quantize(p, 1, 64, 64, 64, 0, 1, p, p, None, None, None)
+    assert st == 5
+    assert L.mx_last_error()

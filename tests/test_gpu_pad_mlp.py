@@ -1,0 +1,92 @@
+"""GPU parity of group padding/unpadding (bit-exact) and of the composed
+MXFP8 MLP steps (dense and routed experts) against the oracle's
+compositions."""
+
+import numpy as np
+import pytest
+import torch
+
+from _helpers import bf16_host, dev, host, to_dev
+from oracle import mx as O
+from quantize_grouped_gemm_amd import mlp, mx, synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("sizes", [[3, 0, 130, 1], [128, 128], [0, 0, 5], [0], [700, 0, 0, 300, 129]])
+def test_pad_unpad(gpu, sizes):
+    sizes = np.array(sizes, np.int32)
+    T = int(sizes.sum())
+    Tcap = synth.capacity(T, len(sizes))
+    rng = np.random.default_rng(T)
+    xb = rng.integers(0, 1 << 16, (T, 96)).astype(np.uint16)
+    x = to_dev(xb.view(np.int16)).view(torch.bfloat16) if T else torch.empty((0, 96), dtype=torch.bfloat16,
+                                                                            device=dev())
+    err = torch.zeros(1, dtype=torch.int32, device=dev())
+    x_pad, offs, src = mx.pad_groups(x, to_dev(sizes), Tcap, dev_err=err)
+    rp, ro, rs = O.pad_groups(xb, sizes, 128, Tcap)
+    np.testing.assert_array_equal(host(offs), ro)
+    np.testing.assert_array_equal(host(src), rs)
+    np.testing.assert_array_equal(bf16_host(x_pad), rp)
+    assert int(err.item()) == 0
+    y = torch.full((T, 96), 7.0, dtype=torch.bfloat16, device=dev())
+    mx.unpad_groups(x_pad, src, T, out=y)
+    np.testing.assert_array_equal(bf16_host(y), xb)
+
+
+def test_pad_invalid_sizes_flag(gpu):
+    x = torch.zeros((10, 32), dtype=torch.bfloat16, device=dev())
+    for sizes, Tcap in (([5, 6], 256), ([-1, 11], 256), ([10, 0], 64)):
+        err = torch.zeros(1, dtype=torch.int32, device=dev())
+        mx.pad_groups(x, to_dev(np.array(sizes, np.int32)), Tcap, dev_err=err, multiple=32 if Tcap == 64 else 128)
+        torch.cuda.synchronize()
+        assert int(err.item()) & 2, sizes
+
+
+def _sqnr(ref, got):
+    ref = np.asarray(ref, np.float64)
+    err = np.asarray(got, np.float64) - ref
+    return 10 * np.log10(np.sum(ref ** 2) / max(np.sum(err ** 2), 1e-300))
+
+
+def test_dense_mlp_step_matches_oracle(gpu):
+    T, D, H = 256, 256, 384
+    x, w1, w3, w2, dy = synth.mlp_inputs(T, D, H, seed=2)
+    net = mlp.DenseMLP(T, D, H, dev())
+    w13 = torch.cat([w1, w3]).to(dev())
+    net.step(x.to(dev()), w13, w2.to(dev()), dy.to(dev()))
+    ref = O.dense_mlp_step(*[synth.bits(t) for t in (x, w1, w3, w2, dy)], "rceil")
+    # z is the first GEMM on bit-exact operands: within 2 bf16 ulp
+    assert _sqnr(O.bf16_to_f64(ref["z"]), O.bf16_to_f64(bf16_host(net.z))) > 50
+    for k, got in (("y", net.y), ("dh", net.dh), ("dx", net.dx)):
+        assert _sqnr(O.bf16_to_f64(ref[k]), O.bf16_to_f64(bf16_host(got))) > 35, k
+    assert _sqnr(ref["dw2"], host(net.dw2)) > 35
+    assert _sqnr(ref["dw13"], host(net.dw13)) > 35
+
+
+@pytest.mark.parametrize("wgrad", ["mx", "hp"])
+def test_moe_mlp_step_matches_oracle(gpu, wgrad):
+    E, T, D, H = 4, 600, 256, 128
+    sizes = np.array([250, 0, 300, 50], np.int32)
+    Tcap = synth.capacity(T, E)
+    x, w1, w3, w2, dy = synth.mlp_inputs(T, D, H, E=E, seed=3)
+    net = mlp.MoEMLP(E, T, D, H, Tcap, dev(), wgrad=wgrad)
+    w13 = torch.cat([w1, w3], dim=1).to(dev())
+    net.step(x.to(dev()), to_dev(sizes), w13, w2.to(dev()), dy.to(dev()))
+    ref = O.moe_mlp_step(*[synth.bits(t) for t in (x,)], sizes, *[synth.bits(t) for t in (w1, w3, w2, dy)],
+                         "rceil", Tcap, wgrad=wgrad)
+    torch.cuda.synchronize()
+    assert int(net.err.item()) == 0
+    np.testing.assert_array_equal(host(net.offs), ref["offs"])
+    for k, got in (("y", net.y), ("dx", net.dx)):
+        assert _sqnr(O.bf16_to_f64(ref[k]), O.bf16_to_f64(bf16_host(got))) > 35, k
+    if wgrad == "mx":
+        dw2, dw13 = host(net.dw2), host(net.dw13)
+        rdw2, rdw13 = ref["dw2"], ref["dw13"]
+    else:
+        dw2, dw13 = O.bf16_to_f64(bf16_host(net.dw2)), O.bf16_to_f64(bf16_host(net.dw13))
+        rdw2, rdw13 = O.bf16_to_f64(ref["dw2"]), O.bf16_to_f64(ref["dw13"])
+    assert np.all(dw2[1] == 0) and np.all(dw13[1] == 0)
+    for g in (0, 2, 3):
+        assert _sqnr(rdw2[g], dw2[g]) > 35
+        assert _sqnr(rdw13[g], dw13[g]) > 35

@@ -1,0 +1,129 @@
+"""GPU parity of MX quantization and dequantization against the oracle:
+bit-exact codes and scales, every direction and mode, ragged tiles, batches,
+strided rows, every finite bf16 value, the stress tensor's planted cases, and
+sampled blocks of the full [32768, 7168] stress tensor."""
+
+import numpy as np
+import pytest
+import torch
+
+from _helpers import bf16_host, dev, host, to_dev
+from oracle import mx as O
+from quantize_grouped_gemm_amd import mx, synth
+
+pytestmark = pytest.mark.gpu
+
+MODES = ["rceil", "floor"]
+
+
+def _check_quant(xb_host, xt, mode, rowwise=True, colwise=True):
+    got = mx.quantize(xt, mode, rowwise, colwise)
+    ref = O.quantize_bf16(xb_host, mode, rowwise, colwise)
+    for k in ref:
+        np.testing.assert_array_equal(host(got[k]), ref[k], err_msg=f"{k} {mode}")
+    return got
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", [(32, 32), (64, 96), (160, 224), (256, 512), (384, 128)])
+def test_quantize_shapes(gpu, mode, shape):
+    xb = synth.bits(synth.stress_tensor(*shape, seed=sum(shape)))
+    _check_quant(xb, to_dev(xb.view(np.int16)).view(torch.bfloat16), mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_quantize_rowwise_any_rows_and_separate_directions(gpu, mode):
+    xb = synth.bits(synth.normal_bf16((100, 96), 1.0, synth.generator(3)))
+    xt = to_dev(xb.view(np.int16)).view(torch.bfloat16)
+    _check_quant(xb, xt, mode, True, False)
+    xb = xb[:96]
+    xt = xt[:96].contiguous()
+    _check_quant(xb, xt, mode, False, True)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_quantize_batched_and_strided(gpu, mode):
+    xb = synth.bits(synth.stress_tensor(3 * 64, 96, seed=11)).reshape(3, 64, 96)
+    _check_quant(xb, to_dev(xb.view(np.int16)).view(torch.bfloat16), mode)
+    # rows with a leading dimension larger than the width (a column slice)
+    wide = synth.bits(synth.stress_tensor(128, 320, seed=12))
+    wt = to_dev(wide.view(np.int16)).view(torch.bfloat16)
+    _check_quant(wide[:, 64:256], wt[:, 64:256], mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_quantize_every_finite_bf16_value(gpu, mode):
+    """Each of the 65280 finite bf16 patterns appears 32 times, in blocks
+    whose other members have log-uniform random magnitudes, so each value is
+    quantized under many different scales."""
+    rng = np.random.default_rng(5)
+    allv = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = allv[(allv & 0x7F80) != 0x7F80]
+    vals = np.tile(finite, 32)
+    rng.shuffle(vals)
+    n = len(vals)
+    cols = 1024
+    rows = -(-n // cols // 32) * 32
+    pad = rows * cols - n
+    filler = (rng.integers(0, 0x7F00, pad) | (rng.integers(0, 2, pad) << 15)).astype(np.uint16)
+    xb = np.concatenate([vals, filler]).reshape(rows, cols)
+    _check_quant(xb, to_dev(xb.view(np.int16)).view(torch.bfloat16), mode)
+
+
+def test_quantize_nonfinite_blocks(gpu):
+    xb = synth.bits(synth.normal_bf16((64, 64), 1.0, synth.generator(9)))
+    xb[3, 5] = 0x7FC0     # NaN
+    xb[40, 33] = 0xFF80   # -inf
+    xb[10, 62] = 0x7F80   # +inf
+    for mode in MODES:
+        _check_quant(xb, to_dev(xb.view(np.int16)).view(torch.bfloat16), mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_stress_full_size_sampled(gpu, mode):
+    """The [32768, 7168] stress tensor, quantized in the launch configuration
+    the benchmark uses. The oracle checks 512 random rows plus every row
+    holding a zero or all-subnormal row block (row-wise), and 256 random
+    columns plus every column holding such a column block (column-wise)."""
+    R, C = synth.STRESS_SHAPE
+    x = synth.stress_tensor(R, C, seed=0, device=dev())
+    got = mx.quantize(x, mode, True, True)
+    rng = np.random.default_rng(1)
+    tiny = 2.0 ** -126
+    a = x.abs().float()
+    special_rows = torch.nonzero((a.view(R, C // 32, 32).amax(-1) < tiny).any(-1)).flatten().cpu().numpy()
+    special_cols = torch.nonzero((a.view(R // 32, 32, C).amax(1) < tiny).any(0)).flatten().cpu().numpy()
+    rows = np.unique(np.concatenate([rng.choice(R, 512, replace=False), special_rows]))
+    cols = np.unique(np.concatenate([rng.choice(C, 256, replace=False), special_cols]))
+    assert len(special_rows) >= 64 and len(special_cols) >= 64
+    ri = torch.as_tensor(rows, device=dev())
+    ci = torch.as_tensor(cols, device=dev())
+    q, s = O.quantize(O.bf16_to_f64(bf16_host(x[ri])), mode)
+    np.testing.assert_array_equal(host(got["q_row"][ri]), q)
+    np.testing.assert_array_equal(host(got["s_row"][ri]), s)
+    q, s = O.quantize(O.bf16_to_f64(bf16_host(x[:, ci])).T, mode)
+    np.testing.assert_array_equal(host(got["q_col"][ci]), q)
+    np.testing.assert_array_equal(host(got["s_col"][ci]), s)
+    # dequantize round trip on the same rows: bit-exact against the oracle
+    deq = mx.dequantize(got["q_row"], got["s_row"], torch.float32)
+    ref = O.f64_to_f32(O.dequantize(host(got["q_row"][ri]), host(got["s_row"][ri])))
+    np.testing.assert_array_equal(host(deq[ri]).view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_dequantize_all_codes_all_scales(gpu, out_dtype):
+    """Every code under every scale byte (0..254 and the NaN scale 0xFF)."""
+    codes = np.tile(np.arange(256, dtype=np.uint8), 256 * 4).reshape(256, 1024)   # [scale byte, ...]
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 32, axis=1)
+    got = mx.dequantize(to_dev(codes), to_dev(scales), out_dtype)
+    ref = O.dequantize(codes, scales)
+    if out_dtype == torch.float32:
+        g = host(got).astype(np.float64)
+        r = O.f64_to_f32(ref).astype(np.float64)
+    else:
+        g = O.bf16_to_f64(bf16_host(got))
+        r = O.bf16_to_f64(O.f64_to_bf16(ref))
+    nan = np.isnan(r)
+    np.testing.assert_array_equal(np.isnan(g), nan)
+    np.testing.assert_array_equal(g[~nan], r[~nan])
+    np.testing.assert_array_equal(np.signbit(g[~nan]), np.signbit(r[~nan]))

@@ -1,0 +1,88 @@
+"""GPU parity of the fused SwiGLU + dual MX quantization kernels (forward and
+backward) against the oracle, plus the fused-vs-standalone contract: the
+fused forward's codes equal the standalone quantization of the bf16 h that
+the same kernel materializes on request."""
+
+import numpy as np
+import pytest
+import torch
+
+from _helpers import bf16_host, code_tolerance, dev, host, to_dev
+from oracle import mx as O
+from quantize_grouped_gemm_amd import mx, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(T, H, seed, scale=2.0):
+    g = synth.generator(seed)
+    z = synth.normal_bf16((T, 2 * H), scale, g)      # the w13 output: [a | b]
+    dh = synth.normal_bf16((T, H), 1.0, g)
+    return synth.bits(z), synth.bits(dh)
+
+
+def _dev_bf16(b):
+    return to_dev(b.view(np.int16)).view(torch.bfloat16)
+
+
+def _assert_close_codes(got, ref, what, frac=1e-5):
+    ndiff, nbeyond, n, nscale = code_tolerance(got[0], got[1], ref[0], ref[1])
+    assert nbeyond == 0, f"{what}: {nbeyond} elements beyond one E4M3 code"
+    assert ndiff <= max(frac * n, 0), f"{what}: {ndiff}/{n} elements differ"
+
+
+@pytest.mark.parametrize("mode", ["rceil", "floor"])
+@pytest.mark.parametrize("T,H", [(64, 96), (160, 224), (2048, 2048)])
+def test_swiglu_fwd(gpu, mode, T, H):
+    zb, _ = _inputs(T, H, seed=T + H)
+    z = _dev_bf16(zb)
+    got = mx.swiglu_quant_fwd(z[:, :H], z[:, H:], mode, want_h=True)
+    ref = O.swiglu_quant_fwd(zb[:, :H], zb[:, H:], mode)
+    _assert_close_codes((host(got["q_row"]), host(got["s_row"])), (ref["q_row"], ref["s_row"]), "row")
+    _assert_close_codes((host(got["q_col"]), host(got["s_col"])), (ref["q_col"], ref["s_col"]), "col")
+    # the materialized bf16 h: within one bf16 ulp of the correctly rounded value
+    hg = O.bf16_to_f64(bf16_host(got["h"]))
+    hr = O.bf16_to_f64(ref["h"])
+    ulp = np.exp2(np.maximum(np.floor(np.log2(np.where(hr != 0, np.abs(hr), 1.0))), -126) - 7)
+    assert np.all(np.abs(hg - hr) <= ulp)
+    assert np.mean(hg != hr) < 1e-3
+    # fused vs standalone: quantizing the kernel's own bf16 h gives the same bytes
+    st = mx.quantize(got["h"], mode, True, True)
+    for k in ("q_row", "s_row", "q_col", "s_col"):
+        assert torch.equal(st[k], got[k]), k
+
+
+@pytest.mark.parametrize("mode", ["rceil", "floor"])
+@pytest.mark.parametrize("T,H", [(64, 96), (160, 224), (2048, 2048)])
+def test_swiglu_bwd(gpu, mode, T, H):
+    zb, dhb = _inputs(T, H, seed=3 * T + H)
+    z = _dev_bf16(zb)
+    dh = _dev_bf16(dhb)
+    got = mx.swiglu_quant_bwd(dh, z[:, :H], z[:, H:], mode, want_dab=True)
+    ref = O.swiglu_quant_bwd(dhb, zb[:, :H], zb[:, H:], mode)
+    _assert_close_codes((host(got["q_row"]), host(got["s_row"])), (ref["q_row"], ref["s_row"]), "row")
+    _assert_close_codes((host(got["q_col"]), host(got["s_col"])), (ref["q_col"], ref["s_col"]), "col")
+    dg = O.bf16_to_f64(bf16_host(got["dab"]))
+    dr = O.bf16_to_f64(ref["dab"])
+    ulp = np.exp2(np.maximum(np.floor(np.log2(np.where(dr != 0, np.abs(dr), 1.0))), -126) - 7)
+    assert np.all(np.abs(dg - dr) <= ulp)
+    st = mx.quantize(got["dab"], mode, True, True)
+    for k in ("q_row", "s_row", "q_col", "s_col"):
+        assert torch.equal(st[k], got[k]), k
+
+
+def test_swiglu_special_values(gpu):
+    """Zero gate or up halves give exact zeros; large |a| saturates silu."""
+    T, H = 64, 64
+    zb, dhb = _inputs(T, H, seed=1)
+    zb[:, :32] = 0                                  # a = 0 -> h = 0, dB = 0
+    zb[:8, H:] = 0                                  # b = 0 -> h = 0
+    zb[8:16, 32:H] = 0xC47A                         # a = -1000
+    zb[16:24, 32:H] = 0x447A                        # a = +1000
+    z = _dev_bf16(zb)
+    got = mx.swiglu_quant_fwd(z[:, :H], z[:, H:], "rceil", want_h=True)
+    ref = O.swiglu_quant_fwd(zb[:, :H], zb[:, H:], "rceil")
+    np.testing.assert_array_equal(bf16_host(got["h"]) & 0x7FFF, ref["h"] & 0x7FFF)
+    for k in ("q_row", "s_row", "q_col", "s_col"):
+        np.testing.assert_array_equal(host(got[k]) & (0x7F if k[0] == "q" else 0xFF),
+                                      ref[k] & (0x7F if k[0] == "q" else 0xFF))
