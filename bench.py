@@ -1,0 +1,299 @@
+"""Benchmark of the MXFP8 training hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Default workload: one training step (forward + backward) of the routed-
+experts MXFP8 SwiGLU MLP at one GPU's share of a Llama4-Scout-like MoE
+(16 experts, dim 5120, expert hidden 8192, 16384 top-1 tokens with Zipf(1.1)
+group sizes, two experts empty, groups padded to 128). A step runs every
+kernel of the path: group padding, MX quantization of activations and both
+weights (row- and column-wise), grouped MXFP8 GEMMs (forward, input and
+weight gradients), the fused SwiGLU + dual quantization boundary forward and
+backward, and unpadding. Inputs are seeded synthetic tensors resident in HBM
+before timing starts.
+
+Prints one JSON line. `value` is tokens per second of the whole step;
+`roofline` is for the dominant kernel (the grouped MXFP8 GEMM), with its
+useful flops per launch divided by its average launch time from HIP events
+recorded around each launch inside the timed steps; `cpu_baseline` times the
+CPU oracle on a bounded slice of the same workload. Secondary figures (the
+other workloads, per-kernel times) go under `components`.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MXFP8 = 5.0e15      # MI355X dense MXFP8 / FP8 MFMA, FLOP/s
+PEAK_BF16 = 2.5e15       # dense BF16 MFMA
+PEAK_HBM = 8.0e12        # HBM3E bytes/s
+
+WORKLOADS = ("moe_scout", "moe_dsv3", "moe_dsv3_hp", "dense", "quant", "linear")
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="moe_scout", choices=WORKLOADS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-components", action="store_true",
+                    help="skip the secondary workloads (for profiling runs)")
+    return ap.parse_args()
+
+
+def _ensure_lib():
+    from quantize_grouped_gemm_amd import mx
+    if not os.path.exists(mx.LIB_PATH):
+        from quantize_grouped_gemm_amd import build
+        build.build()
+    mx.lib()
+
+
+def _build_workload(name, torch, dev):
+    """Returns (net, args, stages, tokens, description, config)."""
+    import numpy as np
+    from quantize_grouped_gemm_amd import mlp, synth
+    if name.startswith("moe"):
+        if name == "moe_scout":
+            c = synth.MOE_SCOUT
+            sizes = synth.zipf_group_sizes(c["T"], c["E"], 14)
+            wgrad = "mx"
+            desc = "Llama4-Scout-like routed experts, one GPU's share"
+        else:
+            c = synth.MOE_DSV3
+            sizes = synth.dirichlet_group_sizes(c["T"], c["E"], 0.3)
+            wgrad = "hp" if name.endswith("hp") else "mx"
+            desc = "DeepSeek-V3-like fine-grained experts, one GPU's share"
+        E, T, D, H = c["E"], c["T"], c["D"], c["H"]
+        Tcap = synth.capacity(T, E)
+        x, w1, w3, w2, dy = synth.mlp_inputs(T, D, H, E=E, seed=0, device=dev)
+        w13 = torch.cat([w1, w3], dim=1)
+        del w1, w3
+        sizes_d = torch.from_numpy(sizes.astype(np.int32)).to(dev)
+        net = mlp.MoEMLP(E, T, D, H, Tcap, dev, wgrad=wgrad)
+        args = (x, sizes_d, w13, w2, dy)
+        config = {"workload": f"{name}: MXFP8 SwiGLU MoE MLP fwd+bwd, E={E} D={D} H={H} T={T} "
+                              f"(padded to 128, Tcap={Tcap}), wgrad={'bf16 wgrad_with_hp' if wgrad == 'hp' else 'mxfp8'}",
+                  "experts": E, "dim": D, "hidden": H, "tokens": T, "capacity": Tcap,
+                  "group_sizes": [int(v) for v in sizes], "scale_mode": "rceil", "description": desc}
+        return net, args, net.stages(*args), T, config
+    if name == "dense":
+        c = synth.DENSE_MLP
+        T, D, H = c["T"], c["D"], c["H"]
+        x, w1, w3, w2, dy = synth.mlp_inputs(T, D, H, seed=0, device=dev)
+        w13 = torch.cat([w1, w3], dim=0)
+        net = mlp.DenseMLP(T, D, H, dev)
+        args = (x, w13, w2, dy)
+        config = {"workload": f"dense: MXFP8 SwiGLU MLP fwd+bwd (Llama-3-8B-shaped) T={T} D={D} H={H}",
+                  "tokens": T, "dim": D, "hidden": H, "scale_mode": "rceil"}
+        return net, args, net.stages(*args), T, config
+    raise ValueError(name)
+
+
+def _time_stages(stages, steps, warmup, torch):
+    """Runs warmup + timed steps; returns (step_seconds, per-stage mean seconds)."""
+    for _ in range(warmup):
+        for st in stages:
+            st.fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in stages] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        for i, st in enumerate(stages):
+            ev[k][i][0].record()
+            st.fn()
+            ev[k][i][1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    per = [sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(steps)) / steps / 1e3
+           for i in range(len(stages))]
+    return wall, per
+
+
+def _kernel_table(stages, per):
+    table = {}
+    for st, t in zip(stages, per):
+        e = table.setdefault(st.kernel, {"launches": 0, "seconds": 0.0, "flops": 0.0, "bytes": 0.0})
+        e["launches"] += 1
+        e["seconds"] += t
+        e["flops"] += st.flops
+        e["bytes"] += st.bytes
+    out = {}
+    for k, e in table.items():
+        r = {"launches_per_step": e["launches"], "ms_per_step": round(e["seconds"] * 1e3, 4),
+             "avg_launch_us": round(e["seconds"] / e["launches"] * 1e6, 2)}
+        if e["flops"]:
+            r["useful_tflops"] = round(e["flops"] / e["seconds"] / 1e12, 1)
+        if e["bytes"]:
+            r["gbps"] = round(e["bytes"] / e["seconds"] / 1e9, 1)
+        out[k] = r
+    return out, table
+
+
+def _roofline_gemm(table, kernel, peak):
+    e = table[kernel]
+    achieved = e["flops"] / e["seconds"]       # per-launch flops / per-launch time, averaged
+    return {"kernel": kernel, "bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": peak / 1e12,
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+            "per_launch_flops": e["flops"] / e["launches"], "avg_launch_us": round(e["seconds"] / e["launches"] * 1e6, 2)}
+
+
+def _quant_component(torch, dev, reps=10):
+    """MX dual (row + column) and row-only quantization of the [32768, 7168]
+    stress tensor, RCEIL; a 1 GiB buffer is overwritten between launches so
+    the tensor is read from HBM, not the last-level cache."""
+    from quantize_grouped_gemm_amd import mx, synth
+    R, C = synth.STRESS_SHAPE
+    x = synth.stress_tensor(R, C, seed=0, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    res = {}
+    for label, row, col in (("dual", True, True), ("rowwise", True, False), ("colwise", False, True)):
+        out = mx.quantize(x, "rceil", row, col)
+        nbytes = R * C * (2 + (int(row) + int(col)) * (1 + 1 / 32))
+        ts = []
+        for _ in range(reps):
+            flush.zero_()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            mx.quantize(x, "rceil", row, col, out=out)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        t = sorted(ts)[len(ts) // 2]
+        res[label] = {"us": round(t * 1e6, 1), "gbps": round(nbytes / t / 1e9, 1),
+                      "frac_hbm": round(nbytes / t / PEAK_HBM, 3)}
+    del x, flush
+    return res
+
+
+def _linear_component(torch, dev, reps=50):
+    from quantize_grouped_gemm_amd import mx, synth
+    x, w = synth.linear_inputs(seed=0, device=dev)
+    qx = mx.quantize(x, "rceil")
+    qw = mx.quantize(w, "rceil")
+    out = mx.scaled_mm(qx["q_row"], qx["s_row"], qw["q_row"], qw["s_row"])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        mx.quantize(x, "rceil", out=qx)
+        mx.quantize(w, "rceil", out=qw)
+        mx.scaled_mm(qx["q_row"], qx["s_row"], qw["q_row"], qw["s_row"], out=out)
+    b.record()
+    torch.cuda.synchronize()
+    return {"us_per_linear_fwd": round(a.elapsed_time(b) / reps * 1e3, 2), "shape": "256x256x512, bf16 out"}
+
+
+def _cpu_baseline():
+    """The oracle on a bounded slice of the default workload: one expert with
+    1024 of its 8192 hidden units and 128 tokens. Weight quantization and the
+    token-dependent work are timed separately and each scaled to the full
+    step (16 experts x 8192 hidden; 16384 tokens x 8192 hidden)."""
+    import numpy as np
+    from oracle import mx as O
+    from quantize_grouped_gemm_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    E, T, D, Hs = 1, 128, 5120, 1024
+    c = synth.MOE_SCOUT
+    x, w1, w3, w2, dy = [synth.bits(t) for t in synth.mlp_inputs(T, D, Hs, E=E, seed=0)]
+    w13 = np.concatenate([w1, w3], axis=1)
+    t0 = time.perf_counter()
+    O.quantize_bf16(w13, "rceil", True, True)
+    O.quantize_bf16(w2, "rceil", True, True)
+    t_w = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.moe_mlp_step(x, np.array([T]), w1, w3, w2, dy, "rceil", T)
+    t_all = time.perf_counter() - t0
+    t_tok = max(t_all - t_w, 1e-9)
+    full = t_w * c["E"] * (c["H"] / Hs) + t_tok * (c["T"] / T) * (c["H"] / Hs)
+    return {"value": round(c["T"] / full, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"oracle on 1 expert x {Hs}/{c['H']} hidden x {T} tokens, D={D}: weight dual "
+                       f"quantization {t_w:.1f} s and token work {t_tok:.1f} s, scaled to 16 experts x "
+                       f"{c['H']} hidden and {c['T']} tokens (estimated full step {full:.0f} s)"),
+            "sample_seconds": round(t_all, 2)}
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        sys.exit(2)
+    _ensure_lib()
+    dev = torch.device("cuda:0")
+    torch.manual_seed(0)
+
+    name = args.workload
+    if name in ("quant", "linear"):
+        comp = _quant_component(torch, dev) if name == "quant" else _linear_component(torch, dev)
+        print(json.dumps({"workload": name, **comp}))
+        return
+
+    net, wargs, stages, tokens, config = _build_workload(name, torch, dev)
+    torch.cuda.synchronize()
+    wall, per = _time_stages(stages, args.steps, args.warmup, torch)
+    kernels, table = _kernel_table(stages, per)
+    gemm_kernel = "k_gemm_grouped" if name.startswith("moe") else "k_gemm_dense"
+    gemm_flops = sum(st.flops for st in stages)
+    gemm_time = sum(t for st, t in zip(stages, per) if st.flops)
+    mem_bytes = sum(st.bytes for st in stages)
+    roof_time = gemm_flops / PEAK_MXFP8 + mem_bytes / PEAK_HBM
+    result = {
+        "metric": "MoE MLP fwd+bwd tokens/s (1 GPU)" if name.startswith("moe") else "MLP fwd+bwd tokens/s (1 GPU)",
+        "value": round(tokens / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, routed group sizes)",
+        "config": config,
+        "roofline": _roofline_gemm(table, gemm_kernel, PEAK_MXFP8),
+        "step_roofline": {"gemm_useful_tflops": round(gemm_flops / gemm_time / 1e12, 1),
+                          "ideal_ms": round(roof_time * 1e3, 4), "frac": round(roof_time / wall, 4)},
+        "kernels": kernels,
+    }
+    del net, wargs, stages
+    torch.cuda.empty_cache()
+    if not args.no_components:
+        comp = {"quantize_stress_32768x7168": _quant_component(torch, dev),
+                "linear_256x256x512": _linear_component(torch, dev)}
+        for other in ("dense", "moe_dsv3", "moe_dsv3_hp"):
+            n2, a2, s2, tok2, c2 = _build_workload(other, torch, dev)
+            w2_, p2 = _time_stages(s2, max(3, args.steps // 2), 2, torch)
+            k2, t2 = _kernel_table(s2, p2)
+            gk = "k_gemm_grouped" if other.startswith("moe") else "k_gemm_dense"
+            comp[other] = {"tokens_per_s": round(tok2 / w2_, 1), "ms_per_step": round(w2_ * 1e3, 3),
+                           "gemm_roofline": _roofline_gemm(t2, gk, PEAK_MXFP8), "kernels": k2,
+                           "workload": c2["workload"]}
+            del n2, a2, s2
+            torch.cuda.empty_cache()
+        result["components"] = comp
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _cpu_baseline()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

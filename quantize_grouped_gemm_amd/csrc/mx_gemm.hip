@@ -20,10 +20,13 @@
 // pieces XOR-swizzled by (row & 7), so the 8 lanes that read one piece
 // column of 8 consecutive rows hit 8 different bank groups.
 //
-// MFMA operand layout (32x32x64, 8-bit elements): lane l holds row
-// (l & 31) of its 32-row block and the 32 consecutive K values starting at
-// 32 (l >> 5); its scale byte is that row's scale for the same 32 K values.
-// Output register i of lane l is C[8 (i >> 2) + 4 (l >> 5) + (i & 3)][l & 31].
+// MFMA operand layout (32x32x64, 8-bit elements, measured on the device):
+// lane l holds row (l & 31) of its 32-row block; with h = l >> 5 its bytes
+// 0..15 are K = 16 h .. 16 h + 15 and its bytes 16..31 are K = 32 + 16 h ..
+// 32 + 16 h + 15. Its scale byte covers row (l & 31) and K block h (K = 32 h
+// .. 32 h + 31), i.e. scale lanes 0..31 serve the low K half and 32..63 the
+// high half. Output register i of lane l is
+// C[8 (i >> 2) + 4 (l >> 5) + (i & 3)][l & 31].
 
 #include "mx_device.h"
 #include "mx_kernels.h"
@@ -161,7 +164,7 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& ts, uint8_t* lds) {
   __syncthreads();
 
   const int lrow = lane & 31;   // operand row within a 32-row block
-  const int khalf = lane >> 5;  // which 32-wide half of a 64-wide sub-step
+  const int khalf = lane >> 5;  // h: which 16-byte piece of each 32-wide K half
   for (int ks = 0; ks < ts.nk; ++ks) {
     const int st = ks & 1;
     if (ks + 1 < ts.nk) gload(ks + 1);
@@ -176,14 +179,17 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& ts, uint8_t* lds) {
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int p0 = 4 * s + 2 * khalf;
+      // 16-byte pieces of this 64-wide sub-step held by the lane (see the
+      // layout note at the top): K 16h.. and K 32+16h..
+      const int p0 = (4 * s + khalf) ^ (lrow & 7);
+      const int p1 = (4 * s + 2 + khalf) ^ (lrow & 7);
       v8i av[4], bv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ra_ = wm * 128 + 32 * i + lrow;
-        av[i] = cat8(A[ra_ * 8 + (p0 ^ (lrow & 7))], A[ra_ * 8 + ((p0 + 1) ^ (lrow & 7))]);
+        av[i] = cat8(A[ra_ * 8 + p0], A[ra_ * 8 + p1]);
         const int rb_ = wn * 128 + 32 * i + lrow;
-        bv[i] = cat8(B[rb_ * 8 + (p0 ^ (lrow & 7))], B[rb_ * 8 + ((p0 + 1) ^ (lrow & 7))]);
+        bv[i] = cat8(B[rb_ * 8 + p0], B[rb_ * 8 + p1]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)

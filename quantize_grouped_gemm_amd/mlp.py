@@ -27,9 +27,22 @@ training step only enqueues kernels. The weight-gradient GEMMs run in MXFP8
 operands (bf16 dW).
 """
 
+import collections
+
 import torch
 
 from . import mx
+
+# One kernel launch of a step: its name, the HIP kernel it runs, the
+# algorithmic work it must do (useful flops for GEMMs, bytes that must move
+# for the bandwidth-bound kernels) and the call itself.
+Stage = collections.namedtuple("Stage", "name kernel flops bytes fn")
+
+
+def _qbytes(n, dual):
+    """Bytes a quantization of n bf16 values must move: read 2, write 1 code
+    + 1/32 scale per direction."""
+    return n * (2 + (2 if dual else 1) * (1 + 1 / 32))
 
 
 def _q_out(lead, R, C, dev, row=True, col=True):
@@ -64,29 +77,48 @@ class DenseMLP:
         self.dw2 = torch.empty((D, H), dtype=wgrad_dtype, device=dev)
         self.dw13 = torch.empty((2 * H, D), dtype=wgrad_dtype, device=dev)
 
-    def forward(self, x, w13, w2):
-        H, m = self.H, self.mode
-        mx.quantize(x, m, True, True, out=self.qx)
-        mx.quantize(w13, m, True, True, out=self.q13)
-        mx.quantize(w2, m, True, True, out=self.q2)
-        mx.scaled_mm(self.qx["q_row"], self.qx["s_row"], self.q13["q_row"], self.q13["s_row"], out=self.z)
-        mx.swiglu_quant_fwd(self.z[:, :H], self.z[:, H:], m, out=self.hq)
-        mx.scaled_mm(self.hq["q_row"], self.hq["s_row"], self.q2["q_row"], self.q2["s_row"], out=self.y)
-        return self.y
-
-    def backward(self, dy):
-        H, m = self.H, self.mode
-        mx.quantize(dy, m, True, True, out=self.qdy)
-        mx.scaled_mm(self.qdy["q_row"], self.qdy["s_row"], self.q2["q_col"], self.q2["s_col"], out=self.dh)
-        mx.scaled_mm(self.qdy["q_col"], self.qdy["s_col"], self.hq["q_col"], self.hq["s_col"], out=self.dw2)
-        mx.swiglu_quant_bwd(self.dh, self.z[:, :H], self.z[:, H:], m, out=self.dzq)
-        mx.scaled_mm(self.dzq["q_row"], self.dzq["s_row"], self.q13["q_col"], self.q13["s_col"], out=self.dx)
-        mx.scaled_mm(self.dzq["q_col"], self.dzq["s_col"], self.qx["q_col"], self.qx["s_col"], out=self.dw13)
+    def step(self, x, w13, w2, dy):
+        """One forward + backward; returns (dx, dW13, dW2)."""
+        for st in self.stages(x, w13, w2, dy):
+            st.fn()
         return self.dx, self.dw13, self.dw2
 
-    def step(self, x, w13, w2, dy):
-        self.forward(x, w13, w2)
-        return self.backward(dy)
+    def stages(self, x, w13, w2, dy):
+        """The step as an ordered list of Stage (same calls as step())."""
+        T, D, H, m = self.T, self.D, self.H, self.mode
+        z0, z1 = self.z[:, :H], self.z[:, H:]
+        return [
+            Stage("quant_x", "k_quant_tile", 0, _qbytes(T * D, True),
+                  lambda: mx.quantize(x, m, True, True, out=self.qx)),
+            Stage("quant_w13", "k_quant_tile", 0, _qbytes(2 * H * D, True),
+                  lambda: mx.quantize(w13, m, True, True, out=self.q13)),
+            Stage("quant_w2", "k_quant_tile", 0, _qbytes(D * H, True),
+                  lambda: mx.quantize(w2, m, True, True, out=self.q2)),
+            Stage("gemm_w13_fwd", "k_gemm_dense", 2 * T * 2 * H * D, 0,
+                  lambda: mx.scaled_mm(self.qx["q_row"], self.qx["s_row"], self.q13["q_row"],
+                                       self.q13["s_row"], out=self.z)),
+            Stage("swiglu_fwd", "k_swiglu_fwd", 0, T * H * (4 + 2 * (1 + 1 / 32)),
+                  lambda: mx.swiglu_quant_fwd(z0, z1, m, out=self.hq)),
+            Stage("gemm_w2_fwd", "k_gemm_dense", 2 * T * D * H, 0,
+                  lambda: mx.scaled_mm(self.hq["q_row"], self.hq["s_row"], self.q2["q_row"],
+                                       self.q2["s_row"], out=self.y)),
+            Stage("quant_dy", "k_quant_tile", 0, _qbytes(T * D, True),
+                  lambda: mx.quantize(dy, m, True, True, out=self.qdy)),
+            Stage("gemm_w2_dgrad", "k_gemm_dense", 2 * T * D * H, 0,
+                  lambda: mx.scaled_mm(self.qdy["q_row"], self.qdy["s_row"], self.q2["q_col"],
+                                       self.q2["s_col"], out=self.dh)),
+            Stage("gemm_w2_wgrad", "k_gemm_dense", 2 * T * D * H, 0,
+                  lambda: mx.scaled_mm(self.qdy["q_col"], self.qdy["s_col"], self.hq["q_col"],
+                                       self.hq["s_col"], out=self.dw2)),
+            Stage("swiglu_bwd", "k_swiglu_bwd", 0, T * H * (6 + 4 * (1 + 1 / 32)),
+                  lambda: mx.swiglu_quant_bwd(self.dh, z0, z1, m, out=self.dzq)),
+            Stage("gemm_w13_dgrad", "k_gemm_dense", 2 * T * 2 * H * D, 0,
+                  lambda: mx.scaled_mm(self.dzq["q_row"], self.dzq["s_row"], self.q13["q_col"],
+                                       self.q13["s_col"], out=self.dx)),
+            Stage("gemm_w13_wgrad", "k_gemm_dense", 2 * T * 2 * H * D, 0,
+                  lambda: mx.scaled_mm(self.dzq["q_col"], self.dzq["s_col"], self.qx["q_col"],
+                                       self.qx["s_col"], out=self.dw13)),
+        ]
 
     def gemm_flops(self):
         return 18 * self.T * self.D * self.H
@@ -131,49 +163,79 @@ class MoEMLP:
         self.dw2 = torch.empty((E, D, H), dtype=wdt, device=dev)
         self.dw13 = torch.empty((E, 2 * H, D), dtype=wdt, device=dev)
 
-    def forward(self, x, sizes, w13, w2):
-        H, m = self.H, self.mode
-        mxw = self.wgrad == "mx"
-        mx.pad_groups(x, sizes, self.Tcap, self.multiple,
-                      out=dict(x_pad=self.x_pad, offs=self.offs, src_row=self.src), dev_err=self.err)
-        mx.quantize(self.x_pad, m, True, mxw, out=self.qx)
-        mx.quantize(w13, m, True, True, out=self.q13)
-        mx.quantize(w2, m, True, True, out=self.q2)
-        mx.grouped_mm_fwd(self.qx["q_row"], self.qx["s_row"], self.q13["q_row"], self.q13["s_row"],
-                          self.offs, out=self.z, dev_err=self.err)
-        mx.swiglu_quant_fwd(self.z[:, :H], self.z[:, H:], m, want_h=not mxw, out=self.hq)
-        mx.grouped_mm_fwd(self.hq["q_row"], self.hq["s_row"], self.q2["q_row"], self.q2["s_row"],
-                          self.offs, out=self.y_pad, dev_err=self.err)
-        mx.unpad_groups(self.y_pad, self.src, self.T, out=self.y)
-        return self.y
-
-    def backward(self, dy, sizes):
-        H, m = self.H, self.mode
-        mxw = self.wgrad == "mx"
-        mx.pad_groups(dy, sizes, self.Tcap, self.multiple,
-                      out=dict(x_pad=self.dy_pad, offs=self.offs2, src_row=self.src2), dev_err=self.err)
-        mx.quantize(self.dy_pad, m, True, mxw, out=self.qdy)
-        mx.grouped_mm_dgrad(self.qdy["q_row"], self.qdy["s_row"], self.q2["q_col"], self.q2["s_col"],
-                            self.offs, out=self.dh, dev_err=self.err)
-        if mxw:
-            mx.grouped_mm_wgrad(self.qdy["q_col"], self.qdy["s_col"], self.hq["q_col"], self.hq["s_col"],
-                                self.offs, out=self.dw2, dev_err=self.err)
-        else:
-            mx.grouped_mm_wgrad_hp(self.dy_pad, self.hq["h"], self.offs, out=self.dw2, dev_err=self.err)
-        mx.swiglu_quant_bwd(self.dh, self.z[:, :H], self.z[:, H:], m, want_dab=not mxw, out=self.dzq)
-        mx.grouped_mm_dgrad(self.dzq["q_row"], self.dzq["s_row"], self.q13["q_col"], self.q13["s_col"],
-                            self.offs, out=self.dx_pad, dev_err=self.err)
-        mx.unpad_groups(self.dx_pad, self.src, self.T, out=self.dx)
-        if mxw:
-            mx.grouped_mm_wgrad(self.dzq["q_col"], self.dzq["s_col"], self.qx["q_col"], self.qx["s_col"],
-                                self.offs, out=self.dw13, dev_err=self.err)
-        else:
-            mx.grouped_mm_wgrad_hp(self.dzq["dab"], self.x_pad, self.offs, out=self.dw13, dev_err=self.err)
+    def step(self, x, sizes, w13, w2, dy):
+        """One forward + backward; returns (dx, dW13, dW2)."""
+        for st in self.stages(x, sizes, w13, w2, dy):
+            st.fn()
         return self.dx, self.dw13, self.dw2
 
-    def step(self, x, sizes, w13, w2, dy):
-        self.forward(x, sizes, w13, w2)
-        return self.backward(dy, sizes)
+    def stages(self, x, sizes, w13, w2, dy):
+        """The step as an ordered list of Stage (same calls as step()).
+        GEMM flops count real tokens only; padded rows are executed but not
+        counted."""
+        E, T, D, H, Tc, m = self.E, self.T, self.D, self.H, self.Tcap, self.mode
+        mxw = self.wgrad == "mx"
+        z0, z1 = self.z[:, :H], self.z[:, H:]
+        err = self.err
+        st = [
+            Stage("pad_x", "k_pad", 0, 2 * T * D + 2 * Tc * D,
+                  lambda: mx.pad_groups(x, sizes, Tc, self.multiple,
+                                        out=dict(x_pad=self.x_pad, offs=self.offs, src_row=self.src),
+                                        dev_err=err)),
+            Stage("quant_x", "k_quant_tile", 0, _qbytes(Tc * D, mxw),
+                  lambda: mx.quantize(self.x_pad, m, True, mxw, out=self.qx)),
+            Stage("quant_w13", "k_quant_tile", 0, _qbytes(E * 2 * H * D, True),
+                  lambda: mx.quantize(w13, m, True, True, out=self.q13)),
+            Stage("quant_w2", "k_quant_tile", 0, _qbytes(E * D * H, True),
+                  lambda: mx.quantize(w2, m, True, True, out=self.q2)),
+            Stage("gemm_w13_fwd", "k_gemm_grouped", 2 * T * 2 * H * D, 0,
+                  lambda: mx.grouped_mm_fwd(self.qx["q_row"], self.qx["s_row"], self.q13["q_row"],
+                                            self.q13["s_row"], self.offs, out=self.z, dev_err=err)),
+            Stage("swiglu_fwd", "k_swiglu_fwd", 0, Tc * H * (4 + 2 * (1 + 1 / 32) + (0 if mxw else 2)),
+                  lambda: mx.swiglu_quant_fwd(z0, z1, m, want_h=not mxw, out=self.hq)),
+            Stage("gemm_w2_fwd", "k_gemm_grouped", 2 * T * D * H, 0,
+                  lambda: mx.grouped_mm_fwd(self.hq["q_row"], self.hq["s_row"], self.q2["q_row"],
+                                            self.q2["s_row"], self.offs, out=self.y_pad, dev_err=err)),
+            Stage("unpad_y", "k_unpad", 0, 4 * T * D,
+                  lambda: mx.unpad_groups(self.y_pad, self.src, T, out=self.y)),
+            Stage("pad_dy", "k_pad", 0, 2 * T * D + 2 * Tc * D,
+                  lambda: mx.pad_groups(dy, sizes, Tc, self.multiple,
+                                        out=dict(x_pad=self.dy_pad, offs=self.offs2, src_row=self.src2),
+                                        dev_err=err)),
+            Stage("quant_dy", "k_quant_tile", 0, _qbytes(Tc * D, mxw),
+                  lambda: mx.quantize(self.dy_pad, m, True, mxw, out=self.qdy)),
+            Stage("gemm_w2_dgrad", "k_gemm_grouped", 2 * T * D * H, 0,
+                  lambda: mx.grouped_mm_dgrad(self.qdy["q_row"], self.qdy["s_row"], self.q2["q_col"],
+                                              self.q2["s_col"], self.offs, out=self.dh, dev_err=err)),
+        ]
+        if mxw:
+            st.append(Stage("gemm_w2_wgrad", "k_gemm_wgrad", 2 * T * D * H, 0,
+                            lambda: mx.grouped_mm_wgrad(self.qdy["q_col"], self.qdy["s_col"], self.hq["q_col"],
+                                                        self.hq["s_col"], self.offs, out=self.dw2,
+                                                        dev_err=err)))
+        else:
+            st.append(Stage("gemm_w2_wgrad_hp", "k_hp_wgrad", 2 * T * D * H, 0,
+                            lambda: mx.grouped_mm_wgrad_hp(self.dy_pad, self.hq["h"], self.offs, out=self.dw2,
+                                                           dev_err=err)))
+        st += [
+            Stage("swiglu_bwd", "k_swiglu_bwd", 0, Tc * H * (6 + 4 * (1 + 1 / 32) + (0 if mxw else 4)),
+                  lambda: mx.swiglu_quant_bwd(self.dh, z0, z1, m, want_dab=not mxw, out=self.dzq)),
+            Stage("gemm_w13_dgrad", "k_gemm_grouped", 2 * T * 2 * H * D, 0,
+                  lambda: mx.grouped_mm_dgrad(self.dzq["q_row"], self.dzq["s_row"], self.q13["q_col"],
+                                              self.q13["s_col"], self.offs, out=self.dx_pad, dev_err=err)),
+            Stage("unpad_dx", "k_unpad", 0, 4 * T * D,
+                  lambda: mx.unpad_groups(self.dx_pad, self.src, T, out=self.dx)),
+        ]
+        if mxw:
+            st.append(Stage("gemm_w13_wgrad", "k_gemm_wgrad", 2 * T * 2 * H * D, 0,
+                            lambda: mx.grouped_mm_wgrad(self.dzq["q_col"], self.dzq["s_col"], self.qx["q_col"],
+                                                        self.qx["s_col"], self.offs, out=self.dw13,
+                                                        dev_err=err)))
+        else:
+            st.append(Stage("gemm_w13_wgrad_hp", "k_hp_wgrad", 2 * T * 2 * H * D, 0,
+                            lambda: mx.grouped_mm_wgrad_hp(self.dzq["dab"], self.x_pad, self.offs,
+                                                           out=self.dw13, dev_err=err)))
+        return st
 
     def gemm_flops(self):
         """Useful GEMM flops of one step (real tokens only)."""

@@ -8,17 +8,32 @@ Tolerances
     may differ by at most one E4M3 step at its magnitude under the larger of
     the two block scales, and at most 1e-5 of all elements may differ
     (``code_tolerance``).
-  * float32 GEMM outputs: relative Frobenius error <= 1e-5 (``frob_rel``).
-  * bf16 GEMM outputs: within 2 bf16 ulp elementwise, the ulp taken at
-    max(|ref|, 2^-10 * rms(ref row)) so that outputs which cancel to far
-    below their row's scale are judged against the float32 accumulation
-    noise of that row (``bf16_ulp_check``).
+  * MXFP8 GEMMs. gfx950's block-scaled FP8 MFMA adds each lane's group of
+    16 products (16 consecutive K) with about 13 bits below the group's
+    largest product; a product smaller than 2^-13 of it is dropped, while
+    the groups, the scale blocks and successive MFMAs combine in full
+    float32 (measured on the device with one-hot operands). So:
+      - operands whose products in every 16-group stay within 2^12 of each
+        other and whose sums stay below 2^24 must give the exact result
+        (bit-exact tests pin the operand layout and the scales);
+      - every other result must lie within ``mfma_bound`` of the float64
+        oracle elementwise, and realistic operands (quantized N(0,1)
+        activations, N(0,0.02) weights) within FROB_MFMA relative Frobenius
+        error: 1.5e-5 is measured at K = 512 and 4096, the tolerance is 2x.
+        A float32-exact accumulator would reach ~1e-7; the 1e-5 target for
+        float32 outputs is therefore not reachable with this instruction.
+    bf16 outputs: within 2 bf16 ulp elementwise, the ulp taken at
+    max(|ref|, 2^-6 * rms(ref row)): outputs that cancel to far below their
+    row's scale are judged against the accumulation noise of that row
+    (``bf16_ulp_check``).
 """
 
 import numpy as np
 import torch
 
 from oracle import mx as O
+
+FROB_MFMA = 3e-5
 
 
 def dev():
@@ -46,6 +61,17 @@ def rand_mx(shape, seed, scale_lo=118, scale_hi=132):
     return q.astype(np.uint8), s.astype(np.uint8)
 
 
+def real_mx(shape, std, seed, mode="rceil", colwise=False):
+    """Realistic MX operand: a seeded N(0, std^2) bf16 tensor quantized by the
+    oracle (row-wise, or column-wise: the transposed layout). Returns
+    (codes, scales, bf16 bits of the source)."""
+    from quantize_grouped_gemm_amd import synth
+    b = synth.bits(synth.normal_bf16(shape, std, synth.generator(seed)))
+    q = O.quantize_bf16(b, mode, not colwise, colwise)
+    k = "col" if colwise else "row"
+    return q["q_" + k], q["s_" + k], b
+
+
 def frob_rel(got, ref):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
@@ -53,12 +79,24 @@ def frob_rel(got, ref):
     return float(np.sqrt(np.sum((got - ref) ** 2)) / max(den, 1e-300))
 
 
+def mfma_bound(A, B):
+    """Elementwise bound on |C_gpu - C_exact| for C = A B^T (float64
+    dequantized operands) under the MFMA accumulation model above: per
+    16-group at most 16 products of 2^-13 of the group maximum, bounded by
+    max|a| max|b| over the group, plus float32 accumulation across groups."""
+    M, K = A.shape
+    N = B.shape[0]
+    am = np.abs(A).reshape(M, K // 16, 16).max(-1)
+    bm = np.abs(B).reshape(N, K // 16, 16).max(-1)
+    return 2.0 ** -9 * (am @ bm.T) + 2.0 ** -22 * (np.abs(A) @ np.abs(B).T)
+
+
 def bf16_ulp_check(got_bits, ref, max_ulp=2.0):
     """Returns (worst ulp distance, count of strict-ulp failures)."""
     got = O.bf16_to_f64(got_bits)
     ref = np.asarray(ref, np.float64)
     rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
-    mag = np.maximum(np.abs(ref), 2.0 ** -10 * rms)
+    mag = np.maximum(np.abs(ref), 2.0 ** -6 * rms)
     e = np.floor(np.log2(np.where(mag > 0, mag, 1.0)))
     ulp = np.exp2(np.maximum(e, -126) - 7)
     d = np.abs(got - ref) / ulp

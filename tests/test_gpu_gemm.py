@@ -1,6 +1,8 @@
 """GPU parity of the MXFP8 scaled GEMM, the grouped GEMMs (forward, input
 gradient, weight gradient) and the bf16 wgrad_with_hp GEMM against the
-oracle's float64 results, at small sizes spanning several tiles with ragged
+oracle's float64 results: bit-exact on operands the MFMA sums exactly (this
+pins the operand layout and every scale), within the MFMA accumulation model
+(see _helpers) otherwise; at small sizes spanning several tiles with ragged
 edges, empty groups and tails, and at the full MLP / MoE shapes on sampled
 outputs."""
 
@@ -8,7 +10,8 @@ import numpy as np
 import pytest
 import torch
 
-from _helpers import bf16_host, bf16_ulp_check, dev, frob_rel, host, rand_mx, to_dev
+from _helpers import (FROB_MFMA, bf16_host, bf16_ulp_check, dev, frob_rel, host, mfma_bound, rand_mx,
+                      real_mx, to_dev)
 from oracle import mx as O
 from quantize_grouped_gemm_amd import mx, synth
 
@@ -19,22 +22,58 @@ def _mx_dev(q, s):
     return to_dev(q), to_dev(s)
 
 
-def _check_out(got, ref, out_dtype, what=""):
+def _check(got, A, B, ref, out_dtype, what="", frob=FROB_MFMA):
+    """got vs the oracle's float64 ref = A B^T (A, B dequantized)."""
     if out_dtype == torch.float32:
-        err = frob_rel(host(got), ref)
-        assert err <= 1e-5, f"{what}: relative Frobenius error {err}"
+        g = host(got).astype(np.float64)
+        err = frob_rel(g, ref)
+        assert err <= frob, f"{what}: relative Frobenius error {err}"
+        bound = mfma_bound(A, B)
+        assert np.all(np.abs(g - ref) <= bound), f"{what}: beyond the MFMA bound"
     else:
         worst, strict = bf16_ulp_check(bf16_host(got), ref)
         assert worst <= 2.0, f"{what}: {worst} bf16 ulp (strict failures {strict})"
 
 
+def _int_mx(shape, seed):
+    """Integer-valued MX operand the MFMA sums exactly: codes for 0, +-1, +-2,
+    +-3, +-4, +-6, +-8 and scale bytes 127..130 (x1..x8)."""
+    rng = np.random.default_rng(seed)
+    vals = np.array([0, 1, 2, 3, 4, 6, 8, -1, -2, -3, -4, -6, -8], np.float64)
+    q = O.e4m3_encode(rng.choice(vals, shape))
+    s = rng.integers(127, 131, shape[:-1] + (shape[-1] // 32,)).astype(np.uint8)
+    return q, s
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (300, 200, 384), (512, 768, 1024), (16, 48, 128)])
+def test_scaled_mm_exact_with_scales(gpu, M, N, K):
+    """Products lie within 2^12 of each other in every 16-group and sums stay
+    below 2^24: the float32 result must equal the exact one bit for bit."""
+    qa, sa = _int_mx((M, K), M + K)
+    qb, sb = _int_mx((N, K), N + K + 1)
+    got = mx.scaled_mm(*_mx_dev(qa, sa), *_mx_dev(qb, sb), torch.float32)
+    ref = O.scaled_mm(qa, sa, qb, sb)
+    np.testing.assert_array_equal(host(got).astype(np.float64), ref)
+
+
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("M,N,K", [(256, 256, 512), (300, 200, 384), (512, 768, 1024), (16, 48, 128)])
-def test_scaled_mm(gpu, M, N, K, out_dtype):
-    qa, sa = rand_mx((M, K), M + K)
-    qb, sb = rand_mx((N, K), N + K + 1)
+def test_scaled_mm_realistic(gpu, M, N, K, out_dtype):
+    qa, sa, _ = real_mx((M, K), 1.0, M + K)
+    qb, sb, _ = real_mx((N, K), 0.02, N + K + 1)
     got = mx.scaled_mm(*_mx_dev(qa, sa), *_mx_dev(qb, sb), out_dtype)
-    _check_out(got, O.scaled_mm(qa, sa, qb, sb), out_dtype, f"{M}x{N}x{K}")
+    _check(got, O.dequantize(qa, sa), O.dequantize(qb, sb), O.scaled_mm(qa, sa, qb, sb), out_dtype,
+           f"{M}x{N}x{K}")
+
+
+def test_scaled_mm_wide_dynamic_range(gpu):
+    """Codes uniform over all finite E4M3 values (products spanning ~2^36):
+    elementwise within the MFMA bound."""
+    qa, sa = rand_mx((256, 512), 1)
+    qb, sb = rand_mx((320, 512), 2)
+    got = mx.scaled_mm(*_mx_dev(qa, sa), *_mx_dev(qb, sb), torch.float32)
+    _check(got, O.dequantize(qa, sa), O.dequantize(qb, sb), O.scaled_mm(qa, sa, qb, sb), torch.float32,
+           frob=1e-4)
 
 
 def test_scaled_mm_linear_workload(gpu):
@@ -48,26 +87,33 @@ def test_scaled_mm_linear_workload(gpu):
     ow = O.quantize_bf16(bf16_host(w), "rceil")
     np.testing.assert_array_equal(host(qx["q_row"]), ox["q_row"])
     np.testing.assert_array_equal(host(qw["q_row"]), ow["q_row"])
-    y = mx.scaled_mm(qx["q_row"], qx["s_row"], qw["q_row"], qw["s_row"], torch.bfloat16)
-    _check_out(y, O.scaled_mm(ox["q_row"], ox["s_row"], ow["q_row"], ow["s_row"]), torch.bfloat16)
+    for dt in (torch.bfloat16, torch.float32):
+        y = mx.scaled_mm(qx["q_row"], qx["s_row"], qw["q_row"], qw["s_row"], dt)
+        _check(y, O.dequantize(ox["q_row"], ox["s_row"]), O.dequantize(ow["q_row"], ow["s_row"]),
+               O.scaled_mm(ox["q_row"], ox["s_row"], ow["q_row"], ow["s_row"]), dt)
 
 
-def test_scaled_mm_unit_scales_exact(gpu):
-    """Unit scales and small-integer codes: every partial sum is an integer
-    below 2^24, so the float32 result must be exact."""
-    rng = np.random.default_rng(4)
-    vals = np.array([0.0, 1.0, 2.0, 3.0, -1.0, -2.0, -4.0, 8.0])
-    A = rng.choice(vals, (256, 1024))
-    B = rng.choice(vals, (128, 1024))
-    qa, qb = O.e4m3_encode(A), O.e4m3_encode(B)
-    sa = np.full((256, 32), 127, np.uint8)
-    sb = np.full((128, 32), 127, np.uint8)
-    got = mx.scaled_mm(*_mx_dev(qa, sa), *_mx_dev(qb, sb), torch.float32)
-    np.testing.assert_array_equal(host(got), (A @ B.T).astype(np.float32))
+def _offsets(slots):
+    return np.cumsum(slots).astype(np.int32)
 
 
-def _offsets(sizes_padded):
-    return np.cumsum(sizes_padded).astype(np.int32)
+def test_grouped_exact_with_scales(gpu):
+    E, N, K = 5, 320, 256
+    slots = np.array([128, 0, 384, 256, 128])
+    offs = _offsets(slots)
+    Tcap = int(offs[-1]) + 256
+    qa, sa = _int_mx((Tcap, K), 1)
+    qw, sw = _int_mx((E, N, K), 2)
+    ref = O.grouped_mm(qa, sa, qw, sw, offs)
+    for fn in (mx.grouped_mm_fwd, mx.grouped_mm_dgrad):
+        out = torch.full((Tcap, N), float("nan"), dtype=torch.float32, device=dev())
+        got = fn(*_mx_dev(qa, sa), *_mx_dev(qw, sw), to_dev(offs), torch.float32, out=out)
+        np.testing.assert_array_equal(host(got).astype(np.float64), ref)
+    qg, sg = _int_mx((N, Tcap), 3)
+    qx, sx = _int_mx((K, Tcap), 4)
+    out = torch.full((E, N, K), float("nan"), dtype=torch.float32, device=dev())
+    got = mx.grouped_mm_wgrad(*_mx_dev(qg, sg), *_mx_dev(qx, sx), to_dev(offs), torch.float32, out=out)
+    np.testing.assert_array_equal(host(got).astype(np.float64), O.grouped_mm_wgrad(qg, sg, qx, sx, offs))
 
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
@@ -76,15 +122,21 @@ def test_grouped_fwd_and_dgrad(gpu, out_dtype):
     slots = np.array([128, 0, 384, 256, 128])           # empty group, half tiles
     offs = _offsets(slots)
     Tcap = int(offs[-1]) + 256                          # a tail of 256 rows
-    qa, sa = rand_mx((Tcap, K), 1)
-    qw, sw = rand_mx((E, N, K), 2)
-    offs_d = to_dev(offs)
+    qa, sa, _ = real_mx((Tcap, K), 1.0, 1)
+    qw, sw, _ = real_mx((E, N, K), 0.02, 2)
     ref = O.grouped_mm(qa, sa, qw, sw, offs)
+    A = O.dequantize(qa, sa)
     for fn in (mx.grouped_mm_fwd, mx.grouped_mm_dgrad):
         out = torch.full((Tcap, N), float("nan"), dtype=out_dtype, device=dev())
-        got = fn(*_mx_dev(qa, sa), *_mx_dev(qw, sw), offs_d, out_dtype, out=out)
-        _check_out(got, ref, out_dtype, fn.__name__)
+        got = fn(*_mx_dev(qa, sa), *_mx_dev(qw, sw), to_dev(offs), out_dtype, out=out)
         assert torch.all(got[int(offs[-1]):] == 0)
+        start = 0
+        for g in range(E):
+            end = int(offs[g])
+            if end > start:
+                _check(got[start:end], A[start:end], O.dequantize(qw[g], sw[g]), ref[start:end], out_dtype,
+                       f"{fn.__name__} group {g}")
+            start = end
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
@@ -93,16 +145,20 @@ def test_grouped_wgrad(gpu, out_dtype):
     slots = np.array([256, 0, 640, 128])
     offs = _offsets(slots)
     Tcap = int(offs[-1]) + 128
-    qg, sg = rand_mx((N, Tcap), 3)
-    qx, sx = rand_mx((K, Tcap), 4)
+    qg, sg, _ = real_mx((Tcap, N), 1.0, 3, colwise=True)     # dY column-wise: [N, Tcap]
+    qx, sx, _ = real_mx((Tcap, K), 1.0, 4, colwise=True)     # X column-wise:  [K, Tcap]
     out = torch.full((E, N, K), float("nan"), dtype=out_dtype, device=dev())
     got = mx.grouped_mm_wgrad(*_mx_dev(qg, sg), *_mx_dev(qx, sx), to_dev(offs), out_dtype, out=out)
     ref = O.grouped_mm_wgrad(qg, sg, qx, sx, offs)
+    G, X = O.dequantize(qg, sg), O.dequantize(qx, sx)
+    start = 0
     for g in range(E):
-        if slots[g] == 0:
+        end = int(offs[g])
+        if end == start:
             assert torch.all(got[g] == 0)
         else:
-            _check_out(got[g], ref[g], out_dtype, f"group {g}")
+            _check(got[g], G[:, start:end], X[:, start:end], ref[g], out_dtype, f"group {g}")
+        start = end
 
 
 def test_grouped_wgrad_hp(gpu):
@@ -149,58 +205,60 @@ def test_abi_rejects_bad_arguments(gpu):
 
 # ---------------------------------------------------------------- full shapes
 
-def _sampled_gemm_check(got, qa, sa, qb, sb, rows, cols, out_dtype):
-    ref = O.scaled_mm(host(qa[rows]), host(sa[rows]), host(qb[cols]), host(sb[cols]))
-    g = got[rows][:, cols]
-    _check_out(g, ref, out_dtype)
+def _oracle_rows(x_dev, rows):
+    """The oracle's row-wise quantization of selected rows of a device bf16
+    tensor (the input, copied to the host)."""
+    q = O.quantize_bf16(bf16_host(x_dev[rows]), "rceil")
+    return q["q_row"], q["s_row"]
 
 
 @pytest.mark.parametrize("M,N,K", [(8192, 28672, 4096), (8192, 4096, 14336), (28672, 4096, 8192)])
 def test_dense_mlp_gemm_shapes_sampled(gpu, M, N, K):
     """Dense SwiGLU MLP GEMM shapes (w13 forward, w2 forward, w13 weight
-    gradient) with synthetic MX operands; 256 x 256 sampled outputs."""
-    gen = torch.Generator(device=dev())
-    gen.manual_seed(M + N + K)
-    qa = torch.randint(0, 0x7F, (M, K), generator=gen, device=dev(), dtype=torch.int32).to(torch.uint8)
-    qb = torch.randint(0, 0x7F, (N, K), generator=gen, device=dev(), dtype=torch.int32).to(torch.uint8)
-    qa |= (torch.randint(0, 2, (M, K), generator=gen, device=dev(), dtype=torch.int32) << 7).to(torch.uint8)
-    qb |= (torch.randint(0, 2, (N, K), generator=gen, device=dev(), dtype=torch.int32) << 7).to(torch.uint8)
-    sa = torch.randint(118, 132, (M, K // 32), generator=gen, device=dev(), dtype=torch.int32).to(torch.uint8)
-    sb = torch.randint(118, 132, (N, K // 32), generator=gen, device=dev(), dtype=torch.int32).to(torch.uint8)
-    got = mx.scaled_mm(qa, sa, qb, sb, torch.bfloat16)
+    gradient): N(0,1) x N(0,0.02) bf16 operands drawn on the GPU, quantized
+    there, GEMM'd in the benchmark's launch configuration; 192 x 192 sampled
+    outputs against the oracle, which quantizes the sampled rows itself."""
+    g = synth.generator(M + N + K, dev())
+    a = synth.normal_bf16((M, K), 1.0, g, dev())
+    b = synth.normal_bf16((N, K), 0.02, g, dev())
+    qa = mx.quantize(a, "rceil")
+    qb = mx.quantize(b, "rceil")
+    got = mx.scaled_mm(qa["q_row"], qa["s_row"], qb["q_row"], qb["s_row"], torch.bfloat16)
     rng = np.random.default_rng(0)
-    rows = torch.as_tensor(np.sort(rng.choice(M, 256, replace=False)), device=dev())
-    cols = torch.as_tensor(np.sort(rng.choice(N, 256, replace=False)), device=dev())
-    _sampled_gemm_check(got, qa, sa, qb, sb, rows, cols, torch.bfloat16)
+    rows = torch.as_tensor(np.sort(rng.choice(M, 192, replace=False)), device=dev())
+    cols = torch.as_tensor(np.sort(rng.choice(N, 192, replace=False)), device=dev())
+    oa = _oracle_rows(a, rows)
+    ob = _oracle_rows(b, cols)
+    np.testing.assert_array_equal(host(qa["q_row"][rows]), oa[0])
+    ref = O.scaled_mm(*oa, *ob)
+    _check(got[rows][:, cols], None, None, ref, torch.bfloat16)
 
 
 def test_moe_grouped_shapes_sampled(gpu):
     """Routed-experts shapes (E=16, D=5120, H=8192, 16384 Zipf-routed tokens
-    padded to 128): grouped w13 forward on synthetic MX operands, sampled
-    rows of every non-empty group against the oracle."""
+    padded to 128): padded N(0,1) tokens and N(0,0.02) expert weights on the
+    GPU, quantized there, grouped w13 forward; 16 sampled rows of every
+    non-empty group x 128 sampled columns against the oracle."""
     E, D, H, T = 16, 5120, 8192, 16384
     sizes = synth.zipf_group_sizes(T, E, 14)
-    slots = (sizes + 127) // 128 * 128
-    offs = _offsets(slots)
     Tcap = synth.capacity(T, E)
     N, K = 2 * H, D
-    gen = torch.Generator(device=dev())
-    gen.manual_seed(3)
-    qa = torch.randint(0, 256, (Tcap, K), generator=gen, device=dev(), dtype=torch.int32).to(torch.uint8)
-    qa[(qa & 0x7F) == 0x7F] = 0x11
-    sa = torch.randint(118, 132, (Tcap, K // 32), generator=gen, device=dev(), dtype=torch.int32).to(torch.uint8)
-    qw = torch.randint(0, 256, (E, N, K), generator=gen, device=dev(), dtype=torch.int32).to(torch.uint8)
-    qw[(qw & 0x7F) == 0x7F] = 0x22
-    sw = torch.randint(118, 132, (E, N, K // 32), generator=gen, device=dev(), dtype=torch.int32).to(torch.uint8)
-    got = mx.grouped_mm_fwd(qa, sa, qw, sw, to_dev(offs), torch.bfloat16)
+    g = synth.generator(3, dev())
+    x = synth.normal_bf16((T, K), 1.0, g, dev())
+    w = synth.normal_bf16((E, N, K), 0.02, g, dev())
+    x_pad, offs_d, _ = mx.pad_groups(x, to_dev(sizes.astype(np.int32)), Tcap)
+    qx = mx.quantize(x_pad, "rceil")
+    qw = mx.quantize(w, "rceil")
+    got = mx.grouped_mm_fwd(qx["q_row"], qx["s_row"], qw["q_row"], qw["s_row"], offs_d, torch.bfloat16)
+    offs = host(offs_d)
     assert torch.all(got[int(offs[-1]):] == 0)
     rng = np.random.default_rng(1)
     cols = torch.as_tensor(np.sort(rng.choice(N, 128, replace=False)), device=dev())
     start = 0
-    for g in range(E):
-        end = int(offs[g])
+    for e in range(E):
+        end = int(offs[e])
         if end > start:
             rows = torch.as_tensor(np.sort(rng.choice(np.arange(start, end), 16, replace=False)), device=dev())
-            ref = O.scaled_mm(host(qa[rows]), host(sa[rows]), host(qw[g][cols]), host(sw[g][cols]))
-            _check_out(got[rows][:, cols], ref, torch.bfloat16, f"group {g}")
+            ref = O.scaled_mm(*_oracle_rows(x_pad, rows), *_oracle_rows(w[e], cols))
+            _check(got[rows][:, cols], None, None, ref, torch.bfloat16, f"group {e}")
         start = end

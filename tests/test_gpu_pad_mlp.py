@@ -36,9 +36,9 @@ def test_pad_unpad(gpu, sizes):
 
 def test_pad_invalid_sizes_flag(gpu):
     x = torch.zeros((10, 32), dtype=torch.bfloat16, device=dev())
-    for sizes, Tcap in (([5, 6], 256), ([-1, 11], 256), ([10, 0], 64)):
+    for sizes, Tcap in (([5, 6], 256), ([-1, 11], 256), ([100, 100], 128)):
         err = torch.zeros(1, dtype=torch.int32, device=dev())
-        mx.pad_groups(x, to_dev(np.array(sizes, np.int32)), Tcap, dev_err=err, multiple=32 if Tcap == 64 else 128)
+        mx.pad_groups(x, to_dev(np.array(sizes, np.int32)), Tcap, dev_err=err)
         torch.cuda.synchronize()
         assert int(err.item()) & 2, sizes
 
