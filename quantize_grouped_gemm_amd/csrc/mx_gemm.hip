@@ -69,27 +69,57 @@ __device__ __forceinline__ v8i cat8(uint4 x, uint4 y) {
   return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
 }
 
-__device__ __forceinline__ void store_tile(const v16f (&acc)[4][4], const TileSpec& ts) {
+// Epilogue: each wave stages its 128 x 128 float sub-tile through LDS in two
+// halves of 64 rows (32 KB per wave per half) and writes whole 16-byte
+// chunks of output rows; only a chunk that crosses valid_n falls back to
+// element stores. The K loop's last barrier has released the LDS.
+__device__ __forceinline__ void store_tile(const v16f (&acc)[4][4], const TileSpec& ts, uint8_t* lds) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
+  float* buf = reinterpret_cast<float*>(lds) + w * (64 * 132);   // [64][128 + 4 pad]
+  const int esz = ts.out_f32 ? 4 : 2;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = wn * 128 + 32 * j + (lane & 31);
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * half + ii;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int row = wm * 128 + 32 * i + 8 * (k >> 2) + 4 * (lane >> 5) + (k & 3);
-        if (row < ts.valid_m && col < ts.valid_n) {
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int r = 32 * ii + 8 * (k >> 2) + 4 * (lane >> 5) + (k & 3);
+          buf[r * 132 + 32 * j + (lane & 31)] = acc[i][j][k];
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    // 64 rows x 128 columns; a lane handles 4 consecutive columns per step
+    const int row0 = wm * 128 + 64 * half;
+    const int col0 = wn * 128;
+#pragma unroll 4
+    for (int e = lane; e < 64 * 32; e += 64) {
+      const int r = e >> 5, c = (e & 31) * 4;
+      const int row = row0 + r, col = col0 + c;
+      if (row >= ts.valid_m || col >= ts.valid_n) continue;
+      const float4 v = *reinterpret_cast<const float4*>(&buf[r * 132 + c]);
+      uint8_t* dst = reinterpret_cast<uint8_t*>(ts.out) + ((int64_t)row * ts.ldo + col) * esz;
+      if (col + 4 <= ts.valid_n) {
+        if (ts.out_f32)
+          *reinterpret_cast<float4*>(dst) = v;
+        else
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+      } else {
+        const float f[4] = {v.x, v.y, v.z, v.w};
+        for (int q = 0; q < ts.valid_n - col; ++q) {
           if (ts.out_f32)
-            reinterpret_cast<float*>(ts.out)[row * ts.ldo + col] = acc[i][j][k];
+            reinterpret_cast<float*>(dst)[q] = f[q];
           else
-            reinterpret_cast<uint16_t*>(ts.out)[row * ts.ldo + col] =
-                (uint16_t)f32_to_bf16(acc[i][j][k]);
+            reinterpret_cast<uint16_t*>(dst)[q] = (uint16_t)f32_to_bf16(f[q]);
         }
       }
     }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -105,52 +135,89 @@ __device__ __forceinline__ void zero_tile(const TileSpec& ts) {
   }
 }
 
+// Operands of one 64-wide K sub-step S (0 or 1) of a 128-wide K step. The
+// lane's two 16-byte pieces are K 16 h.. and K 32 + 16 h.. of the sub-step
+// (h = lane >> 5), XOR-swizzled by the row.
+template <int S>
+__device__ __forceinline__ void load_ops(const uint4* A, const uint4* B, v8i (&av)[4], v8i (&bv)[4],
+                                         int wm, int wn, int lrow, int khalf) {
+  const int p0 = (4 * S + khalf) ^ (lrow & 7);
+  const int p1 = (4 * S + 2 + khalf) ^ (lrow & 7);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra = wm * 128 + 32 * i + lrow;
+    av[i] = cat8(A[ra * 8 + p0], A[ra * 8 + p1]);
+    const int rb = wn * 128 + 32 * i + lrow;
+    bv[i] = cat8(B[rb * 8 + p0], B[rb * 8 + p1]);
+  }
+}
+
+// 4 x 4 MFMAs of sub-step S; its scales are byte 2 S of the shifted scale
+// dwords (see the layout note at the top).
+template <int S>
+__device__ __forceinline__ void mfmas(const v8i (&av)[4], const v8i (&bv)[4], const uint32_t (&sva)[4],
+                                      const uint32_t (&svb)[4], v16f (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = mfma_mx<2 * S>(av[i], bv[j], acc[i][j], sva[i], svb[j]);
+}
+
 __device__ __forceinline__ void gemm_tile(const TileSpec& ts, uint8_t* lds) {
   if (ts.nk <= 0) {
     zero_tile(ts);
     return;
   }
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int w = t >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
 
-  uint4* ldsA = reinterpret_cast<uint4*>(lds);                       // [2][256 rows][8]
-  uint4* ldsB = reinterpret_cast<uint4*>(lds + 2 * kStageA);         // [2][256][8]
-  uint32_t* ldsSA = reinterpret_cast<uint32_t*>(lds + kLdsCodes);    // [2][256]
-  uint32_t* ldsSB = ldsSA + 2 * kBM;                                 // [2][256]
+  const uint4* ldsA = reinterpret_cast<const uint4*>(lds);                  // [2][256 rows][8]
+  const uint4* ldsB = reinterpret_cast<const uint4*>(lds + 2 * kStageA);    // [2][256][8]
+  uint32_t* ldsSA = reinterpret_cast<uint32_t*>(lds + kLdsCodes);           // [2][256]
+  uint32_t* ldsSB = ldsSA + 2 * kBM;                                        // [2][256]
 
-  // global -> register staging: thread t loads 16-byte piece p of rows
-  // r0 + 32 j (j < 8) of both operands, plus one scale dword of row t
-  const int p = t & 7;
-  const int r0 = t >> 3;
-  uint4 ra[8], rb[8];
-  uint32_t rsa, rsb;
-  const int sra = min(t, ts.valid_m - 1);
-  const int srb = min(t, ts.valid_n - 1);
-
-  auto gload = [&](int ks) {
-    const int64_t kb = ts.k_begin + (int64_t)ks * kBK;
+  // Global -> LDS with direct DMA loads (buffer_load_dwordx4 ... lds): each
+  // instruction writes 64 lanes x 16 bytes to consecutive LDS, so one
+  // instruction fills 8 tile rows; wave w fills rows 64 w .. 64 w + 63 of A
+  // and of B. LDS slot (row, s) must hold global piece s ^ (row & 7), so lane
+  // l (row 8 i + (l >> 3), slot l & 7) fetches piece (l & 7) ^ (l >> 3).
+  // The per-lane byte offset is the same for every instruction; the row
+  // block and K step go in the scalar offset. Each operand's buffer resource
+  // ends after its last valid row, so rows past it read as zero.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)ts.a, (short)0, (int)(ts.valid_m * ts.lda), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)ts.b, (short)0, (int)(ts.valid_n * ts.ldb), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rssa = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)ts.sa, (short)0, (int)(ts.valid_m * ts.ldsa), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rssb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)ts.sb, (short)0, (int)(ts.valid_n * ts.ldsb), 0x00020000);
+  const uint32_t voff_a = (lane >> 3) * (uint32_t)ts.lda + 16 * ((lane & 7) ^ (lane >> 3));
+  const uint32_t voff_b = (lane >> 3) * (uint32_t)ts.ldb + 16 * ((lane & 7) ^ (lane >> 3));
+  const uint32_t voff_sa = lane * (uint32_t)ts.ldsa;
+  const uint32_t voff_sb = lane * (uint32_t)ts.ldsb;
+  auto issue = [&](int ks, int st) {
+    const uint32_t kb = (uint32_t)ts.k_begin + (uint32_t)ks * kBK;
+    uint8_t* la = lds + st * kStageA + (64 * wu) * kBK;
+    uint8_t* lb = lds + 2 * kStageA + st * kStageB + (64 * wu) * kBK;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int rowa = min(r0 + 32 * j, ts.valid_m - 1);
-      const int rowb = min(r0 + 32 * j, ts.valid_n - 1);
-      ra[j] = *reinterpret_cast<const uint4*>(ts.a + rowa * ts.lda + kb + 16 * p);
-      rb[j] = *reinterpret_cast<const uint4*>(ts.b + rowb * ts.ldb + kb + 16 * p);
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t row0 = 64 * wu + 8 * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsa, (__attribute__((address_space(3))) void*)(la + i * 1024), 16, voff_a,
+          row0 * (uint32_t)ts.lda + kb, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsb, (__attribute__((address_space(3))) void*)(lb + i * 1024), 16, voff_b,
+          row0 * (uint32_t)ts.ldb + kb, 0, 0);
     }
-    rsa = *reinterpret_cast<const uint32_t*>(ts.sa + sra * ts.ldsa + kb / 32);
-    rsb = *reinterpret_cast<const uint32_t*>(ts.sb + srb * ts.ldsb + kb / 32);
-  };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = r0 + 32 * j;
-      const int slot = row * 8 + (p ^ (row & 7));
-      ldsA[st * (kStageA / 16) + slot] = ra[j];
-      ldsB[st * (kStageB / 16) + slot] = rb[j];
-    }
-    ldsSA[st * kBM + t] = rsa;
-    ldsSB[st * kBN + t] = rsb;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rssa, (__attribute__((address_space(3))) void*)(ldsSA + st * kBM + 64 * wu), 4, voff_sa,
+        64 * wu * (uint32_t)ts.ldsa + kb / 32, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rssb, (__attribute__((address_space(3))) void*)(ldsSB + st * kBN + 64 * wu), 4, voff_sb,
+        64 * wu * (uint32_t)ts.ldsb + kb / 32, 0, 0);
   };
 
   v16f acc[4][4];
@@ -159,49 +226,36 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& ts, uint8_t* lds) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
   const int lrow = lane & 31;   // operand row within a 32-row block
   const int khalf = lane >> 5;  // h: which 16-byte piece of each 32-wide K half
+  v8i a0[4], b0[4], a1[4], b1[4];
+  uint32_t sva[4], svb[4];
+
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   for (int ks = 0; ks < ts.nk; ++ks) {
     const int st = ks & 1;
-    if (ks + 1 < ts.nk) gload(ks + 1);
-
     const uint4* A = ldsA + st * (kStageA / 16);
     const uint4* B = ldsB + st * (kStageB / 16);
-    uint32_t sva[4], svb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       sva[i] = ldsSA[st * kBM + wm * 128 + 32 * i + lrow] >> (8 * khalf);
       svb[i] = ldsSB[st * kBN + wn * 128 + 32 * i + lrow] >> (8 * khalf);
     }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      // 16-byte pieces of this 64-wide sub-step held by the lane (see the
-      // layout note at the top): K 16h.. and K 32+16h..
-      const int p0 = (4 * s + khalf) ^ (lrow & 7);
-      const int p1 = (4 * s + 2 + khalf) ^ (lrow & 7);
-      v8i av[4], bv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ra_ = wm * 128 + 32 * i + lrow;
-        av[i] = cat8(A[ra_ * 8 + p0], A[ra_ * 8 + p1]);
-        const int rb_ = wn * 128 + 32 * i + lrow;
-        bv[i] = cat8(B[rb_ * 8 + p0], B[rb_ * 8 + p1]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = s == 0 ? mfma_mx<0>(av[i], bv[j], acc[i][j], sva[i], svb[j])
-                             : mfma_mx<2>(av[i], bv[j], acc[i][j], sva[i], svb[j]);
-    }
-    if (ks + 1 < ts.nk) sstore(st ^ 1);
+    load_ops<0>(A, B, a0, b0, wm, wn, lrow, khalf);
+    load_ops<1>(A, B, a1, b1, wm, wn, lrow, khalf);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas<0>(a0, b0, sva, svb, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ks + 1 < ts.nk) issue(ks + 1, st ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas<1>(a1, b1, sva, svb, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA into the other stage
     __syncthreads();
   }
-  store_tile(acc, ts);
+  store_tile(acc, ts, lds);
 }
 
 // ---------------------------------------------------------------- groups
