@@ -33,7 +33,7 @@ PEAK_MXFP8 = 5.0e15      # MI355X dense MXFP8 / FP8 MFMA, FLOP/s
 PEAK_BF16 = 2.5e15       # dense BF16 MFMA
 PEAK_HBM = 8.0e12        # HBM3E bytes/s
 
-WORKLOADS = ("moe_scout", "moe_dsv3", "moe_dsv3_hp", "dense", "quant", "linear")
+WORKLOADS = ("moe_scout", "moe_dsv3", "moe_dsv3_hp", "dense", "quant", "linear", "copy")
 
 
 def _args():
@@ -241,6 +241,16 @@ def main():
     torch.manual_seed(0)
 
     name = args.workload
+    if name == "copy":
+        # reference for scaling the FETCH_SIZE / WRITE_SIZE counters: one plain
+        # device copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB)
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30}))
+        return
     if name in ("quant", "linear"):
         comp = _quant_component(torch, dev) if name == "quant" else _linear_component(torch, dev)
         print(json.dumps({"workload": name, **comp}))
