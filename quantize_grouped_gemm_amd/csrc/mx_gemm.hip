@@ -12,13 +12,22 @@
 //                   group's own token range (grouped weight gradient)
 //
 // Tile routine: a 256-thread workgroup computes a 256 x 256 output tile in
-// K steps of 128 (four scale blocks). Waves form a 2 x 2 grid, each owning a
-// 128 x 128 sub-tile = 4 x 4 MFMA blocks of 32 x 32 (256 float accumulators
-// per lane). Per K step the workgroup stages A and B (32 KB each) and their
-// scale dwords in LDS, double-buffered: the global loads of step k+1 are in
-// flight while step k's MFMAs run. LDS rows are 128 bytes with the 16-byte
-// pieces XOR-swizzled by (row & 7), so the 8 lanes that read one piece
-// column of 8 consecutive rows hit 8 different bank groups.
+// K steps of 128 (four scale blocks, two MFMA K sub-steps). Waves form a
+// 2 x 2 grid, each owning a 128 x 128 sub-tile = 4 x 4 MFMA blocks of
+// 32 x 32 (256 float accumulators per lane, in AGPRs). Operands move global
+// -> LDS by direct DMA (buffer_load ... lds) into two stage buffers (66 KB
+// each): the DMA of step k+1 is issued right after the barrier that opens
+// step k, so it has a whole step to land while step k's operands are read
+// from LDS and its 32 MFMAs run. The two buffers are separate LDS objects and
+// the loop is unrolled twice, so the compiler can tell each DMA from the
+// reads it overlaps. LDS rows are 128 bytes with the 16-byte pieces
+// XOR-swizzled by (row & 7): the 8 lanes that read one piece of 8
+// consecutive rows hit 8 different bank groups.
+//
+// Tile order: workgroups are dispatched round-robin over the 8 XCDs, each
+// with its own L2. The linear workgroup index is remapped so that each XCD
+// takes a contiguous run of tiles, and tiles are numbered in bands of 8 row
+// tiles, so the ~32 workgroups resident on one XCD share A and B tiles.
 //
 // MFMA operand layout (32x32x64, 8-bit elements, measured on the device):
 // lane l holds row (l & 31) of its 32-row block; with h = l >> 5 its bytes
@@ -38,11 +47,12 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256, kBN = 256, kBK = 128;
 constexpr int kGemmThreads = 256;
-constexpr int kStageA = kBM * kBK;                     // bytes of codes per stage
-constexpr int kStageB = kBN * kBK;
-constexpr int kLdsCodes = 2 * (kStageA + kStageB);     // 128 KB
-constexpr int kLdsBytes = kLdsCodes + 2 * (kBM + kBN) * 4;
-constexpr int kMaxGroups = 1024;                       // group table lives in LDS
+constexpr int kStageA = kBM * kBK;                       // 32 KB of A codes per stage
+constexpr int kStageB = kBN * kBK;                       // 32 KB of B codes
+constexpr int kStageS = (kBM + kBN) * 4;                 // scale dwords of A and B (2 KB)
+constexpr int kStageBytes = kStageA + kStageB + kStageS;
+constexpr int kBandM = 8;                                // row tiles per band of the tile order
+constexpr int kMaxGroups = 1024;                         // group table lives in LDS
 
 struct TileSpec {
   const uint8_t* a;   // codes of A row 0 of the tile (K index 0)
@@ -69,15 +79,15 @@ __device__ __forceinline__ v8i cat8(uint4 x, uint4 y) {
   return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
 }
 
-// Epilogue: each wave stages its 128 x 128 float sub-tile through LDS in two
-// halves of 64 rows (32 KB per wave per half) and writes whole 16-byte
+// Epilogue: each wave stages its 128 x 128 float sub-tile through its own LDS
+// buffer (one of the ring's stage buffers) in two halves of 64 rows and writes whole 16-byte
 // chunks of output rows; only a chunk that crosses valid_n falls back to
 // element stores. The K loop's last barrier has released the LDS.
 __device__ __forceinline__ void store_tile(const v16f (&acc)[4][4], const TileSpec& ts, uint8_t* lds) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
-  float* buf = reinterpret_cast<float*>(lds) + w * (64 * 132);   // [64][128 + 4 pad]
+  float* buf = reinterpret_cast<float*>(lds);   // this wave's [64][128 + 4 pad]
   const int esz = ts.out_f32 ? 4 : 2;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -135,14 +145,23 @@ __device__ __forceinline__ void zero_tile(const TileSpec& ts) {
   }
 }
 
-// Operands of one 64-wide K sub-step S (0 or 1) of a 128-wide K step. The
-// lane's two 16-byte pieces are K 16 h.. and K 32 + 16 h.. of the sub-step
-// (h = lane >> 5), XOR-swizzled by the row.
+// s_waitcnt immediate waiting until at most n vector-memory operations of
+// this wave are outstanding and all LDS operations are done (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+#define MX_WAIT_VM_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (0x7 << 4))
+
+// Operands of one 64-wide K sub-step S (0 or 1) of a 128-wide K step, read
+// from stage buffer `st`. The lane's two 16-byte pieces are K 16 h.. and
+// K 32 + 16 h.. of the sub-step (h = lane >> 5); row r's piece p sits in slot
+// p ^ (r & 7).
 template <int S>
-__device__ __forceinline__ void load_ops(const uint4* A, const uint4* B, v8i (&av)[4], v8i (&bv)[4],
-                                         int wm, int wn, int lrow, int khalf) {
-  const int p0 = (4 * S + khalf) ^ (lrow & 7);
-  const int p1 = (4 * S + 2 + khalf) ^ (lrow & 7);
+__device__ __forceinline__ void load_ops(const uint8_t* st, v8i (&av)[4], v8i (&bv)[4], int wm, int wn,
+                                         int lane) {
+  const uint4* A = reinterpret_cast<const uint4*>(st);
+  const uint4* B = reinterpret_cast<const uint4*>(st + kStageA);
+  const int lrow = lane & 31, h = lane >> 5;
+  const int p0 = (4 * S + h) ^ (lrow & 7);
+  const int p1 = (4 * S + 2 + h) ^ (lrow & 7);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ra = wm * 128 + 32 * i + lrow;
@@ -152,8 +171,8 @@ __device__ __forceinline__ void load_ops(const uint4* A, const uint4* B, v8i (&a
   }
 }
 
-// 4 x 4 MFMAs of sub-step S; its scales are byte 2 S of the shifted scale
-// dwords (see the layout note at the top).
+// 4 x 4 MFMAs of sub-step S; its scales are byte 2 S of the scale dwords
+// shifted right by 8 h (see the layout note at the top).
 template <int S>
 __device__ __forceinline__ void mfmas(const v8i (&av)[4], const v8i (&bv)[4], const uint32_t (&sva)[4],
                                       const uint32_t (&svb)[4], v16f (&acc)[4][4]) {
@@ -163,7 +182,76 @@ __device__ __forceinline__ void mfmas(const v8i (&av)[4], const v8i (&bv)[4], co
     for (int j = 0; j < 4; ++j) acc[i][j] = mfma_mx<2 * S>(av[i], bv[j], acc[i][j], sva[i], svb[j]);
 }
 
-__device__ __forceinline__ void gemm_tile(const TileSpec& ts, uint8_t* lds) {
+// Barrier between the waves of the workgroup that neither waits for nor
+// orders outstanding DMA (the caller waits with s_waitcnt first); the empty
+// asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+struct TileDma {
+  __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+  uint32_t voff_a, voff_b, voff_sa, voff_sb;
+  uint32_t lda, ldb, ldsa, ldsb;
+  uint32_t k_begin;
+  int wu;
+};
+
+// DMA of K step ks into stage buffer `st`: each instruction writes 64 lanes x
+// 16 bytes to consecutive LDS, i.e. 8 tile rows; wave w fills rows 64 w ..
+// 64 w + 63 of A and of B (8 instructions each) and the scale dwords of those
+// rows. Lane l (row 8 i + (l >> 3), slot l & 7) fetches piece
+// (l & 7) ^ (l >> 3). The per-lane offset is fixed; the row block and K step
+// go in the scalar offset.
+__device__ __forceinline__ void issue_step(const TileDma& d, int ks, uint8_t* st) {
+  const uint32_t kb = d.k_begin + (uint32_t)ks * kBK;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t row0 = 64 * d.wu + 8 * i;
+    uint8_t* rows = st + row0 * kBK;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (__attribute__((address_space(3))) void*)rows, 16,
+                                             d.voff_a, row0 * d.lda + kb, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rb, (__attribute__((address_space(3))) void*)(rows + kStageA), 16,
+                                             d.voff_b, row0 * d.ldb + kb, 0, 0);
+  }
+  uint8_t* sdst = st + kStageA + kStageB + 64 * d.wu * 4;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsa, (__attribute__((address_space(3))) void*)sdst, 4, d.voff_sa,
+                                           64 * d.wu * d.ldsa + kb / 32, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsb, (__attribute__((address_space(3))) void*)(sdst + kBM * 4), 4,
+                                           d.voff_sb, 64 * d.wu * d.ldsb + kb / 32, 0, 0);
+}
+
+// K step ks from stage buffer `cur`; `other` receives step ks+1's DMA.
+__device__ __forceinline__ void k_step(const TileDma& d, int ks, int nk, uint8_t* cur, uint8_t* other,
+                                       v16f (&acc)[4][4], int wm, int wn, int lane) {
+  // this wave's DMA of step ks is done and its reads of step ks-1 (from
+  // `other`) are complete; after the barrier the same holds for all waves
+  MX_WAIT_VM_LDS(0);
+  wg_barrier();
+  if (ks + 1 < nk) issue_step(d, ks + 1, other);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint32_t* SA = reinterpret_cast<const uint32_t*>(cur + kStageA + kStageB);
+  const uint32_t* SB = SA + kBM;
+  const int lrow = lane & 31, h = lane >> 5;
+  uint32_t sva[4], svb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sva[i] = SA[wm * 128 + 32 * i + lrow] >> (8 * h);
+    svb[i] = SB[wn * 128 + 32 * i + lrow] >> (8 * h);
+  }
+  v8i a0[4], b0[4], a1[4], b1[4];
+  load_ops<0>(cur, a0, b0, wm, wn, lane);
+  load_ops<1>(cur, a1, b1, wm, wn, lane);
+  mfmas<0>(a0, b0, sva, svb, acc);
+  mfmas<1>(a1, b1, sva, svb, acc);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void gemm_tile(const TileSpec& ts) {
+  __shared__ __align__(16) uint8_t st0[kStageBytes];
+  __shared__ __align__(16) uint8_t st1[kStageBytes];
   if (ts.nk <= 0) {
     zero_tile(ts);
     return;
@@ -172,53 +260,23 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& ts, uint8_t* lds) {
   const int w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
 
-  const uint4* ldsA = reinterpret_cast<const uint4*>(lds);                  // [2][256 rows][8]
-  const uint4* ldsB = reinterpret_cast<const uint4*>(lds + 2 * kStageA);    // [2][256][8]
-  uint32_t* ldsSA = reinterpret_cast<uint32_t*>(lds + kLdsCodes);           // [2][256]
-  uint32_t* ldsSB = ldsSA + 2 * kBM;                                        // [2][256]
-
-  // Global -> LDS with direct DMA loads (buffer_load_dwordx4 ... lds): each
-  // instruction writes 64 lanes x 16 bytes to consecutive LDS, so one
-  // instruction fills 8 tile rows; wave w fills rows 64 w .. 64 w + 63 of A
-  // and of B. LDS slot (row, s) must hold global piece s ^ (row & 7), so lane
-  // l (row 8 i + (l >> 3), slot l & 7) fetches piece (l & 7) ^ (l >> 3).
-  // The per-lane byte offset is the same for every instruction; the row
-  // block and K step go in the scalar offset. Each operand's buffer resource
-  // ends after its last valid row, so rows past it read as zero.
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)ts.a, (short)0, (int)(ts.valid_m * ts.lda), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)ts.b, (short)0, (int)(ts.valid_n * ts.ldb), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rssa = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)ts.sa, (short)0, (int)(ts.valid_m * ts.ldsa), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rssb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)ts.sb, (short)0, (int)(ts.valid_n * ts.ldsb), 0x00020000);
-  const uint32_t voff_a = (lane >> 3) * (uint32_t)ts.lda + 16 * ((lane & 7) ^ (lane >> 3));
-  const uint32_t voff_b = (lane >> 3) * (uint32_t)ts.ldb + 16 * ((lane & 7) ^ (lane >> 3));
-  const uint32_t voff_sa = lane * (uint32_t)ts.ldsa;
-  const uint32_t voff_sb = lane * (uint32_t)ts.ldsb;
-  auto issue = [&](int ks, int st) {
-    const uint32_t kb = (uint32_t)ts.k_begin + (uint32_t)ks * kBK;
-    uint8_t* la = lds + st * kStageA + (64 * wu) * kBK;
-    uint8_t* lb = lds + 2 * kStageA + st * kStageB + (64 * wu) * kBK;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t row0 = 64 * wu + 8 * i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsa, (__attribute__((address_space(3))) void*)(la + i * 1024), 16, voff_a,
-          row0 * (uint32_t)ts.lda + kb, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsb, (__attribute__((address_space(3))) void*)(lb + i * 1024), 16, voff_b,
-          row0 * (uint32_t)ts.ldb + kb, 0, 0);
-    }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rssa, (__attribute__((address_space(3))) void*)(ldsSA + st * kBM + 64 * wu), 4, voff_sa,
-        64 * wu * (uint32_t)ts.ldsa + kb / 32, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rssb, (__attribute__((address_space(3))) void*)(ldsSB + st * kBN + 64 * wu), 4, voff_sb,
-        64 * wu * (uint32_t)ts.ldsb + kb / 32, 0, 0);
-  };
+  TileDma d;
+  d.wu = __builtin_amdgcn_readfirstlane(w);
+  // each buffer resource ends after the last valid row: rows past it read 0
+  d.ra = __builtin_amdgcn_make_buffer_rsrc((void*)ts.a, (short)0, (int)(ts.valid_m * ts.lda), 0x00020000);
+  d.rb = __builtin_amdgcn_make_buffer_rsrc((void*)ts.b, (short)0, (int)(ts.valid_n * ts.ldb), 0x00020000);
+  d.rsa = __builtin_amdgcn_make_buffer_rsrc((void*)ts.sa, (short)0, (int)(ts.valid_m * ts.ldsa), 0x00020000);
+  d.rsb = __builtin_amdgcn_make_buffer_rsrc((void*)ts.sb, (short)0, (int)(ts.valid_n * ts.ldsb), 0x00020000);
+  d.lda = (uint32_t)ts.lda;
+  d.ldb = (uint32_t)ts.ldb;
+  d.ldsa = (uint32_t)ts.ldsa;
+  d.ldsb = (uint32_t)ts.ldsb;
+  d.k_begin = (uint32_t)ts.k_begin;
+  const uint32_t piece = (lane & 7) ^ (lane >> 3);
+  d.voff_a = (lane >> 3) * d.lda + 16 * piece;
+  d.voff_b = (lane >> 3) * d.ldb + 16 * piece;
+  d.voff_sa = lane * d.ldsa;
+  d.voff_sb = lane * d.ldsb;
 
   v16f acc[4][4];
 #pragma unroll
@@ -226,36 +284,35 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& ts, uint8_t* lds) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-  const int lrow = lane & 31;   // operand row within a 32-row block
-  const int khalf = lane >> 5;  // h: which 16-byte piece of each 32-wide K half
-  v8i a0[4], b0[4], a1[4], b1[4];
-  uint32_t sva[4], svb[4];
-
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int ks = 0; ks < ts.nk; ++ks) {
-    const int st = ks & 1;
-    const uint4* A = ldsA + st * (kStageA / 16);
-    const uint4* B = ldsB + st * (kStageB / 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sva[i] = ldsSA[st * kBM + wm * 128 + 32 * i + lrow] >> (8 * khalf);
-      svb[i] = ldsSB[st * kBN + wn * 128 + 32 * i + lrow] >> (8 * khalf);
-    }
-    load_ops<0>(A, B, a0, b0, wm, wn, lrow, khalf);
-    load_ops<1>(A, B, a1, b1, wm, wn, lrow, khalf);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas<0>(a0, b0, sva, svb, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    if (ks + 1 < ts.nk) issue(ks + 1, st ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas<1>(a1, b1, sva, svb, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA into the other stage
-    __syncthreads();
+  const int nk = ts.nk;
+  issue_step(d, 0, st0);
+  for (int ks = 0; ks < nk; ks += 2) {
+    k_step(d, ks, nk, st0, st1, acc, wm, wn, lane);
+    if (ks + 1 < nk) k_step(d, ks + 1, nk, st1, st0, acc, wm, wn, lane);
   }
-  store_tile(acc, ts, lds);
+  MX_WAIT_VM_LDS(0);
+  wg_barrier();   // every wave is done with the stage buffers
+  uint8_t* mine = (w & 1 ? st1 : st0) + (w >> 1) * (64 * 132 * 4);
+  store_tile(acc, ts, mine);
+}
+
+// Maps the linear index of a workgroup (dispatched round-robin over the 8
+// XCDs) to a tile index so that each XCD gets a contiguous run of tiles.
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  const int xcd = b & 7, j = b >> 3;
+  const int per = total >> 3, rem = total & 7;
+  return xcd * per + min(xcd, rem) + j;
+}
+
+// Tile index -> (row tile, column tile) in bands of kBandM row tiles, column
+// tiles walked within a band.
+__device__ __forceinline__ void band_order(int t, int mt, int nt, int& m, int& n) {
+  const int band = t / (kBandM * nt);
+  const int first = band * kBandM;
+  const int rows = min(kBandM, mt - first);
+  const int r = t - band * kBandM * nt;
+  m = first + r % rows;
+  n = r / rows;
 }
 
 // ---------------------------------------------------------------- groups
@@ -303,9 +360,11 @@ __device__ __forceinline__ int64_t group_start(const int32_t* ends, int g) {
 // ---------------------------------------------------------------- kernels
 
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dense(GemmArgs a) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  const int64_t m0 = (int64_t)blockIdx.y * kBM;
-  const int64_t n0 = (int64_t)blockIdx.x * kBN;
+  const int mt = (int)((a.M + kBM - 1) / kBM), nt = (int)((a.N + kBN - 1) / kBN);
+  int tm, tn;
+  band_order(xcd_remap(blockIdx.x, mt * nt), mt, nt, tm, tn);
+  const int64_t m0 = (int64_t)tm * kBM;
+  const int64_t n0 = (int64_t)tn * kBN;
   TileSpec ts;
   ts.a = a.qa + m0 * a.lda;
   ts.sa = a.sa + m0 * a.ldsa;
@@ -323,20 +382,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dense(GemmArgs a) {
   ts.out = reinterpret_cast<uint8_t*>(a.out) + (m0 * a.ldo + n0) * esz;
   ts.ldo = a.ldo;
   ts.out_f32 = a.out_f32;
-  gemm_tile(ts, lds);
+  gemm_tile(ts);
 }
 
-// blockIdx.y enumerates 256-row tiles of the groups in order (a group of r
-// rows has ceil(r / 256) tiles; the last may hold only 128 rows), followed by
-// the tiles of the tail [ends[E-1], Tcap), which are written as zeros.
+// Row tiles: 256-row tiles of the groups in order (a group of r rows has
+// ceil(r / 256) tiles; the last may hold only 128 rows), followed by the
+// tiles of the tail [ends[E-1], Tcap), which are written as zeros. The grid
+// is an upper bound on row tiles x column tiles; surplus workgroups exit.
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
-  extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int32_t ends[kMaxGroups + 1];
-  __shared__ int32_t tile_end[kMaxGroups + 1];   // inclusive prefix of tile counts
-  const bool reporter = blockIdx.x == 0 && blockIdx.y == 0;
+  __shared__ int32_t tile_end[kMaxGroups + 1];   // inclusive prefix of row-tile counts
+  const bool reporter = blockIdx.x == 0;
   load_group_ends(a.offs, a.E, a.M, ends, a.dev_err, reporter);
   if (threadIdx.x < 64) {
-    // tile counts of groups 0..E (E = the tail), inclusive prefix sum
+    // row-tile counts of groups 0..E (E = the tail), inclusive prefix sum
     const int lane = threadIdx.x;
     int32_t carry = 0;
     for (int g0 = 0; g0 <= a.E; g0 += 64) {
@@ -356,9 +415,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
     if (lane == 0) ends[a.E] = (int32_t)a.M;
   }
   __syncthreads();
-  const int tile = blockIdx.y;
-  if (tile >= tile_end[a.E]) return;
-  // first group whose tile range ends past `tile`
+  const int mt = tile_end[a.E];
+  const int nt = (int)((a.N + kBN - 1) / kBN);
+  if ((int)blockIdx.x >= mt * nt) return;
+  int tile, tn;
+  band_order(xcd_remap(blockIdx.x, mt * nt), mt, nt, tile, tn);
+  // first group whose row-tile range ends past `tile`
   int lo = 0, hi = a.E;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
@@ -368,7 +430,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   const int first = g == 0 ? 0 : tile_end[g - 1];
   const int64_t gs = group_start(ends, g);
   const int64_t m0 = gs + (int64_t)(tile - first) * kBM;
-  const int64_t n0 = (int64_t)blockIdx.x * kBN;
+  const int64_t n0 = (int64_t)tn * kBN;
   TileSpec ts;
   const int gb = min(g, a.E - 1);
   ts.a = a.qa + m0 * a.lda;
@@ -387,19 +449,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   ts.out = reinterpret_cast<uint8_t*>(a.out) + (m0 * a.ldo + n0) * esz;
   ts.ldo = a.ldo;
   ts.out_f32 = a.out_f32;
-  gemm_tile(ts, lds);
+  gemm_tile(ts);
 }
 
-// blockIdx.z ranks the groups by token count (largest first, so the longest
-// tiles are dispatched first); blockIdx.y / x tile dW[g] = [N, K].
+// The grid covers E x (N tiles) x (K tiles) of dW. Tile indices run over the
+// groups ranked by token count, largest first (the longest tiles start
+// first); within a group's [N, K] rectangle tiles follow the band order.
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_wgrad(GemmArgs a) {
-  extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int32_t ends[kMaxGroups + 1];
   __shared__ int32_t pick;
-  const bool reporter = blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0;
-  if (threadIdx.x == 0) pick = min((int)blockIdx.z, a.E - 1);
-  load_group_ends(a.offs, a.E, a.M, ends, a.dev_err, reporter);   // ends with a barrier
-  // group whose rank (descending size, ties by index) equals blockIdx.z
+  const int nt_n = (int)((a.N + kBM - 1) / kBM);
+  const int nt_k = (int)((a.K + kBN - 1) / kBN);
+  const int per = nt_n * nt_k;
+  const int want = (int)blockIdx.x / per;              // group rank
+  const int u = xcd_remap((int)blockIdx.x - want * per, per);
+  if (threadIdx.x == 0) pick = min(want, a.E - 1);
+  load_group_ends(a.offs, a.E, a.M, ends, a.dev_err, blockIdx.x == 0);   // ends with a barrier
+  // group whose rank (descending size, ties by index) equals `want`
   for (int g = threadIdx.x; g < a.E; g += blockDim.x) {
     const int32_t sg = ends[g] - (int32_t)group_start(ends, g);
     int rank = 0;
@@ -407,13 +473,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_wgrad(GemmArgs a) {
       const int32_t sh = ends[h] - (int32_t)group_start(ends, h);
       rank += (sh > sg) || (sh == sg && h < g);
     }
-    if (rank == (int)blockIdx.z) pick = g;
+    if (rank == want) pick = g;
   }
   __syncthreads();
   const int g = pick;
+  int tn, tk;
+  band_order(u, nt_n, nt_k, tn, tk);
   const int64_t ts0 = group_start(ends, g);
-  const int64_t n0 = (int64_t)blockIdx.y * kBM;   // rows of dW = rows of A (= N)
-  const int64_t k0 = (int64_t)blockIdx.x * kBN;   // cols of dW = rows of B (= K)
+  const int64_t n0 = (int64_t)tn * kBM;   // rows of dW = rows of A (= N)
+  const int64_t k0 = (int64_t)tk * kBN;   // cols of dW = rows of B (= K)
   TileSpec ts;
   ts.a = a.qa + n0 * a.lda;
   ts.sa = a.sa + n0 * a.ldsa;
@@ -431,38 +499,29 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_wgrad(GemmArgs a) {
   ts.out = reinterpret_cast<uint8_t*>(a.out) + (g * a.out_group_stride + n0 * a.ldo + k0) * esz;
   ts.ldo = a.ldo;
   ts.out_f32 = a.out_f32;
-  gemm_tile(ts, lds);
+  gemm_tile(ts);
 }
 
 // ---------------------------------------------------------------- launch
 
-static hipError_t set_lds(const void* fn) {
-  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-}
 
 hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s) {
-  hipError_t e = set_lds((const void*)k_gemm_dense);
-  if (e != hipSuccess) return e;
-  dim3 grid((unsigned)((a.N + kBN - 1) / kBN), (unsigned)((a.M + kBM - 1) / kBM));
-  hipLaunchKernelGGL(k_gemm_dense, grid, dim3(kGemmThreads), kLdsBytes, s, a);
+  const int64_t tiles = ((a.N + kBN - 1) / kBN) * ((a.M + kBM - 1) / kBM);
+  hipLaunchKernelGGL(k_gemm_dense, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) {
-  hipError_t e = set_lds((const void*)k_gemm_grouped);
-  if (e != hipSuccess) return e;
   // sum over E groups + tail of ceil(rows / 256) with rows multiples of 128
   const int64_t mtiles = a.M / kBM + (a.E + 2) / 2 + 1;
-  dim3 grid((unsigned)((a.N + kBN - 1) / kBN), (unsigned)mtiles);
-  hipLaunchKernelGGL(k_gemm_grouped, grid, dim3(kGemmThreads), kLdsBytes, s, a);
+  const int64_t tiles = mtiles * ((a.N + kBN - 1) / kBN);
+  hipLaunchKernelGGL(k_gemm_grouped, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_wgrad(const GemmArgs& a, hipStream_t s) {
-  hipError_t e = set_lds((const void*)k_gemm_wgrad);
-  if (e != hipSuccess) return e;
-  dim3 grid((unsigned)((a.K + kBN - 1) / kBN), (unsigned)((a.N + kBM - 1) / kBM), (unsigned)a.E);
-  hipLaunchKernelGGL(k_gemm_wgrad, grid, dim3(kGemmThreads), kLdsBytes, s, a);
+  const int64_t tiles = ((a.K + kBN - 1) / kBN) * ((a.N + kBM - 1) / kBM) * a.E;
+  hipLaunchKernelGGL(k_gemm_wgrad, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a);
   return hipGetLastError();
 }
 
