@@ -20,9 +20,12 @@
 // step k, so it has a whole step to land while step k's operands are read
 // from LDS and its 32 MFMAs run. The two buffers are separate LDS objects and
 // the loop is unrolled twice, so the compiler can tell each DMA from the
-// reads it overlaps. LDS rows are 128 bytes with the 16-byte pieces
-// XOR-swizzled by (row & 7): the 8 lanes that read one piece of 8
-// consecutive rows hit 8 different bank groups.
+// reads it overlaps. LDS rows are 128 bytes; row r's 16-byte piece p sits in
+// slot p ^ f(r) with f(r) = (r & 7) ^ ((r >> 3) & 1). A ds_read_b128 serves
+// 16 lanes (16 consecutive rows, one piece) per pass over the 64 banks
+// (256 bytes): rows of one parity share 128-byte halves, and f takes 8
+// distinct values on the 8 even and on the 8 odd rows of any aligned group
+// of 16, so the pass is free of bank conflicts (and so are 8-lane groups).
 //
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs, each
 // with its own L2. The linear workgroup index is remapped so that each XCD
@@ -153,15 +156,16 @@ __device__ __forceinline__ void zero_tile(const TileSpec& ts) {
 // Operands of one 64-wide K sub-step S (0 or 1) of a 128-wide K step, read
 // from stage buffer `st`. The lane's two 16-byte pieces are K 16 h.. and
 // K 32 + 16 h.. of the sub-step (h = lane >> 5); row r's piece p sits in slot
-// p ^ (r & 7).
+// p ^ f(r) (see the note at the top).
 template <int S>
 __device__ __forceinline__ void load_ops(const uint8_t* st, v8i (&av)[4], v8i (&bv)[4], int wm, int wn,
                                          int lane) {
   const uint4* A = reinterpret_cast<const uint4*>(st);
   const uint4* B = reinterpret_cast<const uint4*>(st + kStageA);
   const int lrow = lane & 31, h = lane >> 5;
-  const int p0 = (4 * S + h) ^ (lrow & 7);
-  const int p1 = (4 * S + 2 + h) ^ (lrow & 7);
+  const int f = (lrow & 7) ^ ((lrow >> 3) & 1);   // rows differ by multiples of 32
+  const int p0 = (4 * S + h) ^ f;
+  const int p1 = (4 * S + 2 + h) ^ f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ra = wm * 128 + 32 * i + lrow;
@@ -193,7 +197,7 @@ __device__ __forceinline__ void wg_barrier() {
 
 struct TileDma {
   __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
-  uint32_t voff_a, voff_b, voff_sa, voff_sb;
+  uint32_t voff_a[2], voff_b[2], voff_sa, voff_sb;
   uint32_t lda, ldb, ldsa, ldsb;
   uint32_t k_begin;
   int wu;
@@ -203,8 +207,9 @@ struct TileDma {
 // 16 bytes to consecutive LDS, i.e. 8 tile rows; wave w fills rows 64 w ..
 // 64 w + 63 of A and of B (8 instructions each) and the scale dwords of those
 // rows. Lane l (row 8 i + (l >> 3), slot l & 7) fetches piece
-// (l & 7) ^ (l >> 3). The per-lane offset is fixed; the row block and K step
-// go in the scalar offset.
+// (l & 7) ^ f(row) = (l & 7) ^ (l >> 3) ^ (i & 1). The per-lane offset takes
+// one of two values (even / odd i); the row block and K step go in the
+// scalar offset.
 __device__ __forceinline__ void issue_step(const TileDma& d, int ks, uint8_t* st) {
   const uint32_t kb = d.k_begin + (uint32_t)ks * kBK;
 #pragma unroll
@@ -212,9 +217,9 @@ __device__ __forceinline__ void issue_step(const TileDma& d, int ks, uint8_t* st
     const uint32_t row0 = 64 * d.wu + 8 * i;
     uint8_t* rows = st + row0 * kBK;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (__attribute__((address_space(3))) void*)rows, 16,
-                                             d.voff_a, row0 * d.lda + kb, 0, 0);
+                                             d.voff_a[i & 1], row0 * d.lda + kb, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rb, (__attribute__((address_space(3))) void*)(rows + kStageA), 16,
-                                             d.voff_b, row0 * d.ldb + kb, 0, 0);
+                                             d.voff_b[i & 1], row0 * d.ldb + kb, 0, 0);
   }
   uint8_t* sdst = st + kStageA + kStageB + 64 * d.wu * 4;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsa, (__attribute__((address_space(3))) void*)sdst, 4, d.voff_sa,
@@ -272,9 +277,12 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& ts) {
   d.ldsa = (uint32_t)ts.ldsa;
   d.ldsb = (uint32_t)ts.ldsb;
   d.k_begin = (uint32_t)ts.k_begin;
-  const uint32_t piece = (lane & 7) ^ (lane >> 3);
-  d.voff_a = (lane >> 3) * d.lda + 16 * piece;
-  d.voff_b = (lane >> 3) * d.ldb + 16 * piece;
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const uint32_t piece = (lane & 7) ^ (lane >> 3) ^ par;
+    d.voff_a[par] = (lane >> 3) * d.lda + 16 * piece;
+    d.voff_b[par] = (lane >> 3) * d.ldb + 16 * piece;
+  }
   d.voff_sa = lane * d.ldsa;
   d.voff_sb = lane * d.ldsb;
 
