@@ -19,12 +19,21 @@
  *    current device) unless stated. The caller owns every buffer; the library
  *    never allocates or frees device memory and keeps no pointer after return.
  *  - bf16 tensors are 16-bit bfloat16; E4M3 codes and E8M0 scales are bytes.
- *    All tensors are row-major. The scales of an [R, C] code tensor are an
- *    [R, C/32] byte tensor (block j of row r covers columns 32j..32j+31), with
- *    no swizzle.
+ *    All tensors are row-major. Block j of row r of an [R, C] code tensor
+ *    covers columns 32j..32j+31; its scale byte is stored in one of two
+ *    layouts (mx_scale_layout):
+ *      MX_SCALES_PLAIN  [R, C/32]: byte r * (C/32) + j;
+ *      MX_SCALES_K128   [C/128, R, 4]: byte ((j/4) * R + r) * 4 + j%4, i.e.
+ *                       for each 128-column step the four block scales of
+ *                       every row form one dword, rows contiguous. Needs
+ *                       C % 128 == 0. The GEMMs read this layout: a tile's
+ *                       scales for one K step are one contiguous run.
+ *    A batch of matrices (or E experts) stores one such tensor per matrix,
+ *    R * C/32 bytes apart, in either layout.
  *  - "Row-wise" quantization blocks the contiguous (last) axis. "Column-wise"
  *    quantization of an [R, C] tensor is row-wise quantization of its
- *    transpose and is stored transposed: codes [C, R], scales [C, R/32].
+ *    transpose and is stored transposed: codes [C, R] with the scales of that
+ *    [C, R] tensor.
  *  - Every GEMM is C = A * B^T with the contraction axis contiguous in both
  *    operands (A [M, K], B [N, K]), float32 accumulation.
  *  - `stream` is a hipStream_t (NULL = the null stream). Every call only
@@ -79,6 +88,9 @@ typedef enum { MX_RCEIL = 0, MX_FLOOR = 1 } mx_scale_mode;
 /* Output element types of GEMMs and dequantization. */
 typedef enum { MX_BF16 = 0, MX_F32 = 1 } mx_dtype;
 
+/* Scale storage layouts (see the conventions above). */
+typedef enum { MX_SCALES_PLAIN = 0, MX_SCALES_K128 = 1 } mx_scale_layout;
+
 /* Direction bits for mx_quantize. */
 enum { MX_ROWWISE = 1, MX_COLWISE = 2 };
 
@@ -98,24 +110,27 @@ mx_status mx_init(void);
  * x: bf16, `batch` matrices of [rows, cols]; element (b, r, c) is at
  *    x[(b * rows + r) * ld + c] (ld >= cols, in elements).
  * dirs: MX_ROWWISE and/or MX_COLWISE. Both together read x once.
- * Row-wise (needs cols % 32 == 0): q_row [batch, rows, cols] codes,
- *    s_row [batch, rows, cols/32] scales.
- * Column-wise (needs rows % 32 == 0): q_col [batch, cols, rows],
- *    s_col [batch, cols, rows/32] (per matrix, i.e. per expert for 3-D
- *    weights).
- * Pointers of a direction not requested may be NULL. */
+ * layout: storage of both directions' scales.
+ * Row-wise (needs cols % 32 == 0, % 128 for MX_SCALES_K128): q_row
+ *    [batch, rows, cols] codes, s_row the scales of each [rows, cols] matrix.
+ * Column-wise (needs rows % 32 == 0, % 128 for MX_SCALES_K128): q_col
+ *    [batch, cols, rows], s_col the scales of each [cols, rows] matrix (per
+ *    expert for 3-D weights).
+ * Pointers of a direction not requested may be NULL; scale pointers must be
+ * 4-byte aligned for MX_SCALES_K128. */
 mx_status mx_quantize(const void* x, int64_t batch, int64_t rows, int64_t cols,
                       int64_t ld, mx_scale_mode mode, unsigned dirs,
-                      uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
-                      uint8_t* s_col, void* stream);
+                      mx_scale_layout layout, uint8_t* q_row, uint8_t* s_row,
+                      uint8_t* q_col, uint8_t* s_col, void* stream);
 
-/* Dequantization: out[r, c] = E4M3(q[r, c]) * 2^(s[r, c/32] - 127), exact in
- * float32 (out_dtype MX_F32) or rounded to nearest-even bf16 (MX_BF16).
- * A NaN code or a 0xFF scale gives NaN. q [rows, cols], s [rows, cols/32],
- * out [rows, cols] contiguous; cols % 32 == 0. */
+/* Dequantization: out[r, c] = E4M3(q[r, c]) * 2^(scale(r, c/32) - 127),
+ * exact in float32 (out_dtype MX_F32) or rounded to nearest-even bf16
+ * (MX_BF16). A NaN code or a 0xFF scale gives NaN. q [rows, cols], s in
+ * `layout`, out [rows, cols] contiguous; cols % 32 == 0 (% 128 for
+ * MX_SCALES_K128). */
 mx_status mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows,
-                        int64_t cols, mx_dtype out_dtype, void* out,
-                        void* stream);
+                        int64_t cols, mx_scale_layout layout,
+                        mx_dtype out_dtype, void* out, void* stream);
 
 /* Fused SwiGLU + dual MXFP8 quantization, forward ([P3], Summary).
  * a, b: bf16 [rows, hidden], row stride ld_ab elements: the gate half (w1
@@ -123,35 +138,40 @@ mx_status mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows,
  *    [rows, 2*hidden] output pass a = base, b = base + hidden, ld_ab = 2*hidden.
  * h = silu(a) * b is evaluated in float32, rounded to bf16 (the tensor the
  * unfused path would hold; it is not written unless h_out is non-NULL) and
- * quantized twice:
- *    row-wise along hidden:  q_row [rows, hidden], s_row [rows, hidden/32]
- *    column-wise along rows: q_col [hidden, rows], s_col [hidden, rows/32]
+ * quantized twice (scales in `layout`):
+ *    row-wise along hidden:  q_row [rows, hidden], s_row of [rows, hidden]
+ *    column-wise along rows: q_col [hidden, rows], s_col of [hidden, rows]
  * h_out: optional bf16 [rows, hidden] copy of h (NULL to skip); used by the
- *    wgrad_with_hp recipe. Needs rows % 32 == 0 and hidden % 32 == 0. */
+ *    wgrad_with_hp recipe. Needs rows % 32 == 0 and hidden % 32 == 0 (both
+ *    % 128 for MX_SCALES_K128). */
 mx_status mx_swiglu_quant_fwd(const void* a, const void* b, int64_t ld_ab,
                               int64_t rows, int64_t hidden, mx_scale_mode mode,
-                              uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
-                              uint8_t* s_col, void* h_out, void* stream);
+                              mx_scale_layout layout, uint8_t* q_row,
+                              uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                              void* h_out, void* stream);
 
 /* Fused SwiGLU backward + dual MXFP8 quantization ([P3], Summary).
  * dh: bf16 [rows, hidden], row stride ld_dh (gradient of h, from the w2
  *    input-gradient GEMM); a, b as in the forward.
  * With s = sigmoid(a): dA = dh*b*s*(1 + a*(1-s)), dB = dh*a*s, in float32,
- * rounded to bf16, laid out as dZ = [dA | dB] [rows, 2*hidden] and quantized:
- *    row-wise along 2*hidden: q_row [rows, 2*hidden], s_row [rows, 2*hidden/32]
- *    column-wise along rows:  q_col [2*hidden, rows], s_col [2*hidden, rows/32]
+ * rounded to bf16, laid out as dZ = [dA | dB] [rows, 2*hidden] and quantized
+ * (scales in `layout`):
+ *    row-wise along 2*hidden: q_row [rows, 2*hidden], s_row of [rows, 2*hidden]
+ *    column-wise along rows:  q_col [2*hidden, rows], s_col of [2*hidden, rows]
  * dab_out: optional bf16 [rows, 2*hidden] copy of dZ (NULL to skip).
- * Needs rows % 32 == 0 and hidden % 32 == 0. */
+ * Needs rows % 32 == 0 and hidden % 32 == 0 (both % 128 for MX_SCALES_K128). */
 mx_status mx_swiglu_quant_bwd(const void* dh, int64_t ld_dh, const void* a,
                               const void* b, int64_t ld_ab, int64_t rows,
                               int64_t hidden, mx_scale_mode mode,
-                              uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
-                              uint8_t* s_col, void* dab_out, void* stream);
+                              mx_scale_layout layout, uint8_t* q_row,
+                              uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                              void* dab_out, void* stream);
 
 /* MXFP8 scaled GEMM for the linear override ([P1], Autograd function
  * changes: _to_mxfp8_then_scaled_mm). out[m, n] = sum_k A[m,k] * B[n,k] with
- * A = deq(qa [M, K], sa [M, K/32]) and B = deq(qb [N, K], sb [N, K/32]),
- * float32 accumulation, then rounded to out_dtype (bf16: nearest-even).
+ * A = deq(qa [M, K], sa) and B = deq(qb [N, K], sb), scales in the
+ * MX_SCALES_K128 layout (4-byte aligned), float32 accumulation, then
+ * rounded to out_dtype (bf16: nearest-even).
  * out row stride ld_out elements (>= N). K % 128 == 0; M, N >= 1.
  * The same call serves the forward, the input gradient (A = dY row-wise,
  * B = W column-wise) and the weight gradient (A = dY column-wise, B = X
@@ -163,8 +183,9 @@ mx_status mx_scaled_mm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb,
 
 /* MXFP8 grouped GEMM, 2-D x 3-D, forward ([P1], Tensor subclass changes:
  * the grouped_mm override; [P3], Summary: the grouped MLP GEMMs).
- * qa [Tcap, K], sa [Tcap, K/32]: tokens in padded expert-major order.
- * qw [E, N, K], sw [E, N, K/32]: per-expert weights quantized along K.
+ * qa [Tcap, K], sa: tokens in padded expert-major order.
+ * qw [E, N, K], sw: per-expert weights quantized along K.
+ * All scales in the MX_SCALES_K128 layout (per expert for sw).
  * offs: device int32 [E] (see the conventions above).
  * out [Tcap, N] (out_dtype): rows of group g are A_g * W_g^T; rows at or past
  * offs[E-1] are written as zeros. K % 128 == 0, N % 16 == 0, Tcap % 128 == 0.
@@ -189,8 +210,8 @@ mx_status mx_scaled_grouped_mm_dgrad(const uint8_t* qa, const uint8_t* sa,
 
 /* MXFP8 grouped GEMM, weight gradient, 2-D x 2-D: the contraction runs over
  * each group's own tokens. dW[g] = deq(G^T)[:, s_g:e_g] * deq(X^T)[:, s_g:e_g]^T
- * qg [N, Tcap], sg [N, Tcap/32]: dY column-wise (quantized along tokens).
- * qx [K, Tcap], sx [K, Tcap/32]: X column-wise.
+ * qg [N, Tcap], sg: dY column-wise (quantized along tokens).
+ * qx [K, Tcap], sx: X column-wise. Scales in the MX_SCALES_K128 layout.
  * out [E, N, K] (out_dtype); an empty group's slice is written as zeros.
  * N % 16 == 0, K % 16 == 0, Tcap % 128 == 0. */
 mx_status mx_scaled_grouped_mm_wgrad(const uint8_t* qg, const uint8_t* sg,

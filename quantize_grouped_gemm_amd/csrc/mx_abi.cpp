@@ -24,6 +24,10 @@ mx_status fail(mx_status st, const char* fmt, ...) {
 }
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// The GEMMs address a K128 scale matrix with 32-bit buffer offsets.
+bool scales_fit(int64_t rows, int64_t k) { return rows * (k / 32) < (1ll << 31); }
 
 // 0 = unknown, 1 = gfx950, -1 = other
 int g_dev_ok[64];
@@ -65,17 +69,23 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 extern "C" {
 
-int mx_abi_version(void) { return 1; }
+int mx_abi_version(void) { return 2; }
 
 const char* mx_last_error(void) { return g_err; }
 
 mx_status mx_init(void) { return check_device(); }
 
 mx_status mx_quantize(const void* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
-                      mx_scale_mode mode, unsigned dirs, uint8_t* q_row, uint8_t* s_row,
-                      uint8_t* q_col, uint8_t* s_col, void* stream) {
+                      mx_scale_mode mode, unsigned dirs, mx_scale_layout layout, uint8_t* q_row,
+                      uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, void* stream) {
   MX_REQUIRE(mode == MX_RCEIL || mode == MX_FLOOR, MX_ERR_ARG, "mx_quantize: bad scale mode %d", (int)mode);
   MX_REQUIRE(dirs != 0 && (dirs & ~3u) == 0, MX_ERR_ARG, "mx_quantize: dirs must be MX_ROWWISE|MX_COLWISE");
+  MX_REQUIRE(layout == MX_SCALES_PLAIN || layout == MX_SCALES_K128, MX_ERR_ARG, "mx_quantize: bad scale layout");
+  const bool k128 = layout == MX_SCALES_K128;
+  MX_REQUIRE(!k128 || !(dirs & MX_ROWWISE) || cols % 128 == 0, MX_ERR_SHAPE,
+             "mx_quantize: K128 row-wise scales need cols (%lld) to be a multiple of 128", (long long)cols);
+  MX_REQUIRE(!k128 || !(dirs & MX_COLWISE) || rows % 128 == 0, MX_ERR_SHAPE,
+             "mx_quantize: K128 column-wise scales need rows (%lld) to be a multiple of 128", (long long)rows);
   MX_REQUIRE(batch >= 0 && rows >= 0 && cols >= 0, MX_ERR_SHAPE, "mx_quantize: negative size");
   MX_REQUIRE(cols % 32 == 0, MX_ERR_SHAPE, "mx_quantize: cols (%lld) must be a multiple of 32", (long long)cols);
   MX_REQUIRE(!(dirs & MX_COLWISE) || rows % 32 == 0, MX_ERR_SHAPE,
@@ -88,46 +98,56 @@ mx_status mx_quantize(const void* x, int64_t batch, int64_t rows, int64_t cols, 
   if (dirs & MX_ROWWISE) {
     MX_REQUIRE(q_row && s_row, MX_ERR_NULL, "mx_quantize: q_row/s_row NULL");
     MX_REQUIRE(al16(q_row), MX_ERR_ALIGN, "mx_quantize: q_row must be 16-byte aligned");
+    MX_REQUIRE(!k128 || al4(s_row), MX_ERR_ALIGN, "mx_quantize: K128 s_row must be 4-byte aligned");
   }
   if (dirs & MX_COLWISE) {
     MX_REQUIRE(q_col && s_col, MX_ERR_NULL, "mx_quantize: q_col/s_col NULL");
     MX_REQUIRE(al16(q_col), MX_ERR_ALIGN, "mx_quantize: q_col must be 16-byte aligned");
+    MX_REQUIRE(!k128 || al4(s_col), MX_ERR_ALIGN, "mx_quantize: K128 s_col must be 4-byte aligned");
   }
   MX_DEVICE();
-  mxk::QuantArgs a{static_cast<const uint16_t*>(x), rows, cols, ld, mode == MX_RCEIL,
+  mxk::QuantArgs a{static_cast<const uint16_t*>(x), rows, cols, ld, mode == MX_RCEIL, k128,
                    (dirs & MX_ROWWISE) ? q_row : nullptr, (dirs & MX_ROWWISE) ? s_row : nullptr,
                    (dirs & MX_COLWISE) ? q_col : nullptr, (dirs & MX_COLWISE) ? s_col : nullptr};
   return launched(mxk::launch_quant(a, batch, as_stream(stream)), "mx_quantize");
 }
 
 mx_status mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols,
-                        mx_dtype out_dtype, void* out, void* stream) {
+                        mx_scale_layout layout, mx_dtype out_dtype, void* out, void* stream) {
   MX_REQUIRE(out_dtype == MX_BF16 || out_dtype == MX_F32, MX_ERR_ARG, "mx_dequantize: bad dtype");
-  MX_REQUIRE(rows >= 0 && cols >= 0 && cols % 32 == 0, MX_ERR_SHAPE, "mx_dequantize: cols must be a multiple of 32");
+  MX_REQUIRE(layout == MX_SCALES_PLAIN || layout == MX_SCALES_K128, MX_ERR_ARG, "mx_dequantize: bad scale layout");
+  const bool k128 = layout == MX_SCALES_K128;
+  MX_REQUIRE(rows >= 0 && cols >= 0 && cols % (k128 ? 128 : 32) == 0, MX_ERR_SHAPE,
+             "mx_dequantize: cols must be a multiple of 32 (128 for K128 scales)");
   if (rows == 0 || cols == 0) return MX_OK;
   MX_REQUIRE(q && s && out, MX_ERR_NULL, "mx_dequantize: NULL pointer");
   MX_REQUIRE(al16(q) && al16(out), MX_ERR_ALIGN, "mx_dequantize: q/out must be 16-byte aligned");
   MX_DEVICE();
-  mxk::DequantArgs a{q, s, rows, cols, out_dtype == MX_F32, out};
+  mxk::DequantArgs a{q, s, rows, cols, out_dtype == MX_F32, k128, out};
   return launched(mxk::launch_dequant(a, as_stream(stream)), "mx_dequantize");
 }
 
 static mx_status check_swiglu_common(const char* fn, int64_t rows, int64_t hidden, mx_scale_mode mode,
-                                     uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col) {
+                                     mx_scale_layout layout, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                                     uint8_t* s_col) {
   MX_REQUIRE(mode == MX_RCEIL || mode == MX_FLOOR, MX_ERR_ARG, "%s: bad scale mode", fn);
-  MX_REQUIRE(rows >= 0 && hidden >= 0 && rows % 32 == 0 && hidden % 32 == 0, MX_ERR_SHAPE,
-             "%s: rows and hidden must be non-negative multiples of 32", fn);
+  MX_REQUIRE(layout == MX_SCALES_PLAIN || layout == MX_SCALES_K128, MX_ERR_ARG, "%s: bad scale layout", fn);
+  const int64_t m = layout == MX_SCALES_K128 ? 128 : 32;
+  MX_REQUIRE(rows >= 0 && hidden >= 0 && rows % m == 0 && hidden % m == 0, MX_ERR_SHAPE,
+             "%s: rows and hidden must be non-negative multiples of %lld", fn, (long long)m);
   MX_REQUIRE((rows + 127) / 128 <= 65535, MX_ERR_SHAPE, "%s: too many rows for one launch", fn);
   if (rows == 0 || hidden == 0) return MX_OK;
   MX_REQUIRE(q_row && s_row && q_col && s_col, MX_ERR_NULL, "%s: NULL output", fn);
   MX_REQUIRE(al16(q_row) && al16(q_col), MX_ERR_ALIGN, "%s: code outputs must be 16-byte aligned", fn);
+  MX_REQUIRE(m == 32 || (al4(s_row) && al4(s_col)), MX_ERR_ALIGN, "%s: K128 scales must be 4-byte aligned", fn);
   return MX_OK;
 }
 
 mx_status mx_swiglu_quant_fwd(const void* a, const void* b, int64_t ld_ab, int64_t rows, int64_t hidden,
-                              mx_scale_mode mode, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
-                              uint8_t* s_col, void* h_out, void* stream) {
-  mx_status st = check_swiglu_common("mx_swiglu_quant_fwd", rows, hidden, mode, q_row, s_row, q_col, s_col);
+                              mx_scale_mode mode, mx_scale_layout layout, uint8_t* q_row, uint8_t* s_row,
+                              uint8_t* q_col, uint8_t* s_col, void* h_out, void* stream) {
+  mx_status st =
+      check_swiglu_common("mx_swiglu_quant_fwd", rows, hidden, mode, layout, q_row, s_row, q_col, s_col);
   if (st != MX_OK || rows == 0 || hidden == 0) return st;
   MX_REQUIRE(a && b, MX_ERR_NULL, "mx_swiglu_quant_fwd: a/b NULL");
   MX_REQUIRE(al16(a) && al16(b) && ld_ab >= hidden && ld_ab % 8 == 0, MX_ERR_ALIGN,
@@ -135,14 +155,17 @@ mx_status mx_swiglu_quant_fwd(const void* a, const void* b, int64_t ld_ab, int64
   MX_REQUIRE(!h_out || al16(h_out), MX_ERR_ALIGN, "mx_swiglu_quant_fwd: h_out must be 16-byte aligned");
   MX_DEVICE();
   mxk::SwigluFwdArgs k{static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), ld_ab, rows, hidden,
-                       mode == MX_RCEIL, q_row, s_row, q_col, s_col, static_cast<uint16_t*>(h_out)};
+                       mode == MX_RCEIL, layout == MX_SCALES_K128, q_row, s_row, q_col, s_col,
+                       static_cast<uint16_t*>(h_out)};
   return launched(mxk::launch_swiglu_fwd(k, as_stream(stream)), "mx_swiglu_quant_fwd");
 }
 
 mx_status mx_swiglu_quant_bwd(const void* dh, int64_t ld_dh, const void* a, const void* b, int64_t ld_ab,
-                              int64_t rows, int64_t hidden, mx_scale_mode mode, uint8_t* q_row,
-                              uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, void* dab_out, void* stream) {
-  mx_status st = check_swiglu_common("mx_swiglu_quant_bwd", rows, hidden, mode, q_row, s_row, q_col, s_col);
+                              int64_t rows, int64_t hidden, mx_scale_mode mode, mx_scale_layout layout,
+                              uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, void* dab_out,
+                              void* stream) {
+  mx_status st =
+      check_swiglu_common("mx_swiglu_quant_bwd", rows, hidden, mode, layout, q_row, s_row, q_col, s_col);
   if (st != MX_OK || rows == 0 || hidden == 0) return st;
   MX_REQUIRE(dh && a && b, MX_ERR_NULL, "mx_swiglu_quant_bwd: dh/a/b NULL");
   MX_REQUIRE(al16(dh) && al16(a) && al16(b) && ld_ab >= hidden && ld_ab % 8 == 0 && ld_dh >= hidden &&
@@ -152,14 +175,14 @@ mx_status mx_swiglu_quant_bwd(const void* dh, int64_t ld_dh, const void* a, cons
   MX_DEVICE();
   mxk::SwigluBwdArgs k{static_cast<const uint16_t*>(dh), static_cast<const uint16_t*>(a),
                        static_cast<const uint16_t*>(b), ld_dh, ld_ab, rows, hidden, mode == MX_RCEIL,
-                       q_row, s_row, q_col, s_col, static_cast<uint16_t*>(dab_out)};
+                       layout == MX_SCALES_K128, q_row, s_row, q_col, s_col, static_cast<uint16_t*>(dab_out)};
   return launched(mxk::launch_swiglu_bwd(k, as_stream(stream)), "mx_swiglu_quant_bwd");
 }
 
 static mx_status check_mx_operand(const char* fn, const char* name, const uint8_t* q, const uint8_t* s) {
   MX_REQUIRE(q && s, MX_ERR_NULL, "%s: %s codes/scales NULL", fn, name);
   MX_REQUIRE(al16(q), MX_ERR_ALIGN, "%s: %s codes must be 16-byte aligned", fn, name);
-  MX_REQUIRE((reinterpret_cast<uintptr_t>(s) & 3u) == 0, MX_ERR_ALIGN, "%s: %s scales must be 4-byte aligned", fn, name);
+  MX_REQUIRE(al4(s), MX_ERR_ALIGN, "%s: %s scales must be 4-byte aligned", fn, name);
   return MX_OK;
 }
 
@@ -176,6 +199,7 @@ mx_status mx_scaled_mm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
   MX_REQUIRE(out_dtype == MX_BF16 || out_dtype == MX_F32, MX_ERR_ARG, "%s: bad dtype", fn);
   MX_REQUIRE(M >= 0 && N >= 0 && K > 0 && K % 128 == 0, MX_ERR_SHAPE, "%s: K (%lld) must be a positive multiple of 128", fn, (long long)K);
   MX_REQUIRE((M + 255) / 256 <= 65535 && (N + 255) / 256 <= 65535, MX_ERR_SHAPE, "%s: M or N too large", fn);
+  MX_REQUIRE(scales_fit(M, K) && scales_fit(N, K), MX_ERR_SHAPE, "%s: scale matrices too large", fn);
   if (M == 0 || N == 0) return MX_OK;
   MX_CHECK(check_mx_operand(fn, "A", qa, sa));
   MX_CHECK(check_mx_operand(fn, "B", qb, sb));
@@ -187,7 +211,7 @@ mx_status mx_scaled_mm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
   mxk::GemmArgs a{};
   a.qa = qa; a.sa = sa; a.qb = qb; a.sb = sb;
   a.M = M; a.N = N; a.K = K;
-  a.lda = K; a.ldb = K; a.ldsa = K / 32; a.ldsb = K / 32;
+  a.lda = K; a.ldb = K; a.srows_a = M; a.srows_b = N;
   a.out = out; a.ldo = ld_out; a.out_f32 = out_dtype == MX_F32;
   return launched(mxk::launch_gemm_dense(a, as_stream(stream)), fn);
 }
@@ -201,6 +225,7 @@ static mx_status grouped_2d3d(const char* fn, const uint8_t* qa, const uint8_t* 
   MX_REQUIRE(N > 0 && N % 16 == 0, MX_ERR_SHAPE, "%s: N must be a positive multiple of 16", fn);
   MX_REQUIRE(K > 0 && K % 128 == 0, MX_ERR_SHAPE, "%s: K must be a positive multiple of 128", fn);
   MX_REQUIRE(Tcap / 256 + E <= 65535 && (N + 255) / 256 <= 65535, MX_ERR_SHAPE, "%s: too large", fn);
+  MX_REQUIRE(scales_fit(Tcap, K) && scales_fit(N, K), MX_ERR_SHAPE, "%s: scale matrices too large", fn);
   if (Tcap == 0) return MX_OK;
   MX_CHECK(check_mx_operand(fn, "A", qa, sa));
   MX_CHECK(check_mx_operand(fn, "W", qw, sw));
@@ -210,7 +235,7 @@ static mx_status grouped_2d3d(const char* fn, const uint8_t* qa, const uint8_t* 
   mxk::GemmArgs a{};
   a.qa = qa; a.sa = sa; a.qb = qw; a.sb = sw;
   a.M = Tcap; a.N = N; a.K = K;
-  a.lda = K; a.ldb = K; a.ldsa = K / 32; a.ldsb = K / 32;
+  a.lda = K; a.ldb = K; a.srows_a = Tcap; a.srows_b = N;
   a.b_group_stride = N * K; a.sb_group_stride = N * (K / 32);
   a.out = out; a.ldo = N; a.out_f32 = out_dtype == MX_F32;
   a.offs = offs; a.E = E; a.dev_err = dev_err;
@@ -242,6 +267,7 @@ mx_status mx_scaled_grouped_mm_wgrad(const uint8_t* qg, const uint8_t* sg, const
   MX_REQUIRE(Tcap >= 0 && Tcap % 128 == 0, MX_ERR_SHAPE, "%s: Tcap must be a multiple of 128", fn);
   MX_REQUIRE(N > 0 && N % 16 == 0 && K > 0 && K % 16 == 0, MX_ERR_SHAPE, "%s: N and K must be positive multiples of 16", fn);
   MX_REQUIRE((N + 255) / 256 <= 65535 && (K + 255) / 256 <= 65535, MX_ERR_SHAPE, "%s: too large", fn);
+  MX_REQUIRE(scales_fit(N, Tcap) && scales_fit(K, Tcap), MX_ERR_SHAPE, "%s: scale matrices too large", fn);
   MX_CHECK(check_mx_operand(fn, "G", qg, sg));
   MX_CHECK(check_mx_operand(fn, "X", qx, sx));
   MX_REQUIRE(offs && out, MX_ERR_NULL, "%s: offs/out NULL", fn);
@@ -250,7 +276,7 @@ mx_status mx_scaled_grouped_mm_wgrad(const uint8_t* qg, const uint8_t* sg, const
   mxk::GemmArgs a{};
   a.qa = qg; a.sa = sg; a.qb = qx; a.sb = sx;
   a.M = Tcap; a.N = N; a.K = K;
-  a.lda = Tcap; a.ldb = Tcap; a.ldsa = Tcap / 32; a.ldsb = Tcap / 32;
+  a.lda = Tcap; a.ldb = Tcap; a.srows_a = N; a.srows_b = K;
   a.out_group_stride = N * K;
   a.out = out; a.ldo = K; a.out_f32 = out_dtype == MX_F32;
   a.offs = offs; a.E = E; a.dev_err = dev_err;

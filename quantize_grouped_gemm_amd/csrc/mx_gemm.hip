@@ -56,13 +56,21 @@ constexpr int kStageS = (kBM + kBN) * 4;                 // scale dwords of A an
 constexpr int kStageBytes = kStageA + kStageB + kStageS;
 constexpr int kBandM = 8;                                // row tiles per band of the tile order
 constexpr int kMaxGroups = 1024;                         // group table lives in LDS
+#ifndef MX_GEMM_PREFETCH
+#define MX_GEMM_PREFETCH 1
+#endif
+constexpr bool kPrefetch = MX_GEMM_PREFETCH;             // L2 prefetch two steps ahead of the DMA
+constexpr int kDmaOps = 18;                              // vector-memory ops of one step's DMA per wave
+constexpr int kPfOps = kPrefetch ? 2 : 0;                // and of one step's prefetch
 
 struct TileSpec {
   const uint8_t* a;   // codes of A row 0 of the tile (K index 0)
-  const uint8_t* sa;  // scales of A row 0
+  const uint8_t* sa;  // k128 scale dword of A row 0, K step 0
   const uint8_t* b;
   const uint8_t* sb;
-  int64_t lda, ldb, ldsa, ldsb;
+  int64_t lda, ldb;
+  int64_t sstep_a, sstep_b;   // scale bytes per K step (4 x scale rows)
+  int64_t sbytes_a, sbytes_b; // scale bytes from sa / sb to the end of the scale matrix
   int valid_m, valid_n;  // A rows / B rows that exist in this tile (1..256)
   int64_t k_begin;       // first contraction index, multiple of 128
   int nk;                // number of 128-wide K steps (0 => C = 0)
@@ -197,8 +205,9 @@ __device__ __forceinline__ void wg_barrier() {
 
 struct TileDma {
   __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
-  uint32_t voff_a[2], voff_b[2], voff_sa, voff_sb;
-  uint32_t lda, ldb, ldsa, ldsb;
+  uint32_t voff_a[2], voff_b[2];
+  uint32_t voff_pa, voff_pb;   // prefetch: row (64 w + lane) of A / of B
+  uint32_t lda, ldb, sstep_a, sstep_b;
   uint32_t k_begin;
   int wu;
 };
@@ -209,7 +218,9 @@ struct TileDma {
 // rows. Lane l (row 8 i + (l >> 3), slot l & 7) fetches piece
 // (l & 7) ^ f(row) = (l & 7) ^ (l >> 3) ^ (i & 1). The per-lane offset takes
 // one of two values (even / odd i); the row block and K step go in the
-// scalar offset.
+// scalar offset. The scales of a K step are 256 consecutive dwords per
+// operand (k128 layout): wave w copies dwords 64 w .. 64 w + 63 of each, two
+// 128-byte lines per instruction.
 __device__ __forceinline__ void issue_step(const TileDma& d, int ks, uint8_t* st) {
   const uint32_t kb = d.k_begin + (uint32_t)ks * kBK;
 #pragma unroll
@@ -222,41 +233,102 @@ __device__ __forceinline__ void issue_step(const TileDma& d, int ks, uint8_t* st
                                              d.voff_b[i & 1], row0 * d.ldb + kb, 0, 0);
   }
   uint8_t* sdst = st + kStageA + kStageB + 64 * d.wu * 4;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsa, (__attribute__((address_space(3))) void*)sdst, 4, d.voff_sa,
-                                           64 * d.wu * d.ldsa + kb / 32, 0, 0);
+  const uint32_t lane4 = (threadIdx.x & 63) * 4;
+  const uint32_t kstep = kb / kBK;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsa, (__attribute__((address_space(3))) void*)sdst, 4, lane4,
+                                           kstep * d.sstep_a + 256 * d.wu, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsb, (__attribute__((address_space(3))) void*)(sdst + kBM * 4), 4,
-                                           d.voff_sb, 64 * d.wu * d.ldsb + kb / 32, 0, 0);
+                                           lane4, kstep * d.sstep_b + 256 * d.wu, 0, 0);
 }
 
-// K step ks from stage buffer `cur`; `other` receives step ks+1's DMA.
-__device__ __forceinline__ void k_step(const TileDma& d, int ks, int nk, uint8_t* cur, uint8_t* other,
-                                       v16f (&acc)[4][4], int wm, int wn, int lane) {
-  // this wave's DMA of step ks is done and its reads of step ks-1 (from
-  // `other`) are complete; after the barrier the same holds for all waves
-  MX_WAIT_VM_LDS(0);
-  wg_barrier();
-  if (ks + 1 < nk) issue_step(d, ks + 1, other);
-  __builtin_amdgcn_sched_barrier(0);
-  const uint32_t* SA = reinterpret_cast<const uint32_t*>(cur + kStageA + kStageB);
+// L2 prefetch of K step ks: one 4-byte load per lane per operand touches
+// the 128-byte line that holds row (64 w + lane)'s K chunk of the step, so
+// that the step's DMA, issued two steps later, finds its lines in L2. The
+// loads go to a scratch LDS area that is never read: they need no register
+// and are not removed as dead.
+__device__ __forceinline__ void prefetch_step(const TileDma& d, int ks, uint8_t* sink) {
+  const uint32_t kb = d.k_begin + (uint32_t)ks * kBK;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (__attribute__((address_space(3))) void*)sink, 4, d.voff_pa,
+                                           64 * d.wu * d.lda + kb, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rb, (__attribute__((address_space(3))) void*)sink, 4, d.voff_pb,
+                                           64 * d.wu * d.ldb + kb, 0, 0);
+}
+
+// Scale dwords of the lane's A and B row blocks in stage buffer `st`: byte
+// 2 S + h of each serves sub-step S (after the shift by 8 h).
+__device__ __forceinline__ void load_scales(const uint8_t* st, uint32_t (&sva)[4], uint32_t (&svb)[4], int wm,
+                                            int wn, int lane) {
+  const uint32_t* SA = reinterpret_cast<const uint32_t*>(st + kStageA + kStageB);
   const uint32_t* SB = SA + kBM;
   const int lrow = lane & 31, h = lane >> 5;
-  uint32_t sva[4], svb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     sva[i] = SA[wm * 128 + 32 * i + lrow] >> (8 * h);
     svb[i] = SB[wn * 128 + 32 * i + lrow] >> (8 * h);
   }
-  v8i a0[4], b0[4], a1[4], b1[4];
-  load_ops<0>(cur, a0, b0, wm, wn, lane);
-  load_ops<1>(cur, a1, b1, wm, wn, lane);
-  mfmas<0>(a0, b0, sva, svb, acc);
-  mfmas<1>(a1, b1, sva, svb, acc);
+}
+
+struct Regs {
+  v8i a0[4], b0[4], a1[4], b1[4];   // operands of sub-steps 0 and 1
+  uint32_t sva[4], svb[4];          // scales of the step being multiplied
+  uint32_t nsa[4], nsb[4];          // scales of the next step
+};
+
+// Interleaving hints: within the next scheduling region, alternate one MFMA
+// with `ds` LDS reads and `vm` vector-memory instructions.
+template <int DS, int VM>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (DS > 0) __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
+    if constexpr (VM > 0) __builtin_amdgcn_sched_group_barrier(0x010, VM, 0);
+  }
+}
+
+// One K step ks held in stage buffer `cur`; sub-step 0's
+// operands and the step's scales are in registers. Step ks+1 is in flight to
+// `nxt` (its DMA is followed by exactly two prefetch loads).
+//   1. sub-step 0's MFMAs run while sub-step 1's operands are read from `cur`;
+//   2. wait until this wave's DMA of step ks+1 has landed and its LDS reads
+//      are done, then barrier: `cur` is free and `nxt` is complete for all
+//      waves;
+//   3. the DMA of step ks+2 into `cur` (the last step, once past the end:
+//      it is never read) and the L2 prefetch of step ks+4 are issued while
+//      sub-step 1's MFMAs run and step ks+1's sub-step 0 operands and scales
+//      are read from `nxt`.
+// The MFMA unit thus sees no gap for LDS latency or DMA issue; only the
+// barrier itself lies between the two halves. The last step runs the same
+// code: its DMA rewrites a free buffer and its reads of `nxt` go unused,
+// which keeps a single register assignment for the accumulators.
+__device__ __forceinline__ void step_full(const TileDma& d, int ks, int nk, uint8_t* cur, uint8_t* nxt, Regs& r,
+                                          v16f (&acc)[4][4], int wm, int wn, int lane, uint8_t* sink) {
   __builtin_amdgcn_sched_barrier(0);
+  mfmas<0>(r.a0, r.b0, r.sva, r.svb, acc);
+  load_ops<1>(cur, r.a1, r.b1, wm, wn, lane);
+  interleave<1, 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  MX_WAIT_VM_LDS(kPfOps);
+  wg_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  issue_step(d, ks + 2 < nk ? ks + 2 : nk - 1, cur);
+  if constexpr (kPrefetch) prefetch_step(d, ks + 4 < nk ? ks + 4 : nk - 1, sink);
+  mfmas<1>(r.a1, r.b1, r.sva, r.svb, acc);
+  load_ops<0>(nxt, r.a0, r.b0, wm, wn, lane);
+  load_scales(nxt, r.nsa, r.nsb, wm, wn, lane);
+  interleave<2, 2>();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r.sva[i] = r.nsa[i];
+    r.svb[i] = r.nsb[i];
+  }
 }
 
 __device__ __forceinline__ void gemm_tile(const TileSpec& ts) {
   __shared__ __align__(16) uint8_t st0[kStageBytes];
   __shared__ __align__(16) uint8_t st1[kStageBytes];
+  __shared__ __align__(16) uint8_t sink[256];
   if (ts.nk <= 0) {
     zero_tile(ts);
     return;
@@ -270,12 +342,15 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& ts) {
   // each buffer resource ends after the last valid row: rows past it read 0
   d.ra = __builtin_amdgcn_make_buffer_rsrc((void*)ts.a, (short)0, (int)(ts.valid_m * ts.lda), 0x00020000);
   d.rb = __builtin_amdgcn_make_buffer_rsrc((void*)ts.b, (short)0, (int)(ts.valid_n * ts.ldb), 0x00020000);
-  d.rsa = __builtin_amdgcn_make_buffer_rsrc((void*)ts.sa, (short)0, (int)(ts.valid_m * ts.ldsa), 0x00020000);
-  d.rsb = __builtin_amdgcn_make_buffer_rsrc((void*)ts.sb, (short)0, (int)(ts.valid_n * ts.ldsb), 0x00020000);
+  // scale rows past the valid ones hold other rows' scales (or read 0 past
+  // the end of the matrix): they only meet zero operand rows, whose
+  // outputs are not stored
+  d.rsa = __builtin_amdgcn_make_buffer_rsrc((void*)ts.sa, (short)0, (int)ts.sbytes_a, 0x00020000);
+  d.rsb = __builtin_amdgcn_make_buffer_rsrc((void*)ts.sb, (short)0, (int)ts.sbytes_b, 0x00020000);
   d.lda = (uint32_t)ts.lda;
   d.ldb = (uint32_t)ts.ldb;
-  d.ldsa = (uint32_t)ts.ldsa;
-  d.ldsb = (uint32_t)ts.ldsb;
+  d.sstep_a = (uint32_t)ts.sstep_a;
+  d.sstep_b = (uint32_t)ts.sstep_b;
   d.k_begin = (uint32_t)ts.k_begin;
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
@@ -283,8 +358,8 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& ts) {
     d.voff_a[par] = (lane >> 3) * d.lda + 16 * piece;
     d.voff_b[par] = (lane >> 3) * d.ldb + 16 * piece;
   }
-  d.voff_sa = lane * d.ldsa;
-  d.voff_sb = lane * d.ldsb;
+  d.voff_pa = lane * d.lda;
+  d.voff_pb = lane * d.ldb;
 
   v16f acc[4][4];
 #pragma unroll
@@ -293,11 +368,26 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& ts) {
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
   const int nk = ts.nk;
+  const int last = nk - 1;
+  // prologue: steps 0 and 1 to LDS, each DMA followed by two prefetch loads
+  // (steps 2 and 3; past the end, the last step stands in)
   issue_step(d, 0, st0);
-  for (int ks = 0; ks < nk; ks += 2) {
-    k_step(d, ks, nk, st0, st1, acc, wm, wn, lane);
-    if (ks + 1 < nk) k_step(d, ks + 1, nk, st1, st0, acc, wm, wn, lane);
+  if constexpr (kPrefetch) prefetch_step(d, 2 < nk ? 2 : last, sink);
+  issue_step(d, 1 < nk ? 1 : last, st1);
+  if constexpr (kPrefetch) prefetch_step(d, 3 < nk ? 3 : last, sink);
+  MX_WAIT_VM_LDS(kDmaOps + 2 * kPfOps);   // step 0 has landed (step 1's DMA and the prefetches may not)
+  wg_barrier();
+  Regs r;
+  load_ops<0>(st0, r.a0, r.b0, wm, wn, lane);
+  load_scales(st0, r.sva, r.svb, wm, wn, lane);
+  // pairs of steps, then an odd last step: every path into a step on st0
+  // has waited for st0's DMA at the barrier before
+  int ks = 0;
+  for (; ks + 1 < nk; ks += 2) {
+    step_full(d, ks, nk, st0, st1, r, acc, wm, wn, lane, sink);
+    step_full(d, ks + 1, nk, st1, st0, r, acc, wm, wn, lane, sink);
   }
+  if (ks < nk) step_full(d, ks, nk, st0, st1, r, acc, wm, wn, lane, sink);
   MX_WAIT_VM_LDS(0);
   wg_barrier();   // every wave is done with the stage buffers
   uint8_t* mine = (w & 1 ? st1 : st0) + (w >> 1) * (64 * 132 * 4);
@@ -374,18 +464,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dense(GemmArgs a) {
   const int64_t m0 = (int64_t)tm * kBM;
   const int64_t n0 = (int64_t)tn * kBN;
   TileSpec ts;
+  const int64_t steps = a.K / kBK;
   ts.a = a.qa + m0 * a.lda;
-  ts.sa = a.sa + m0 * a.ldsa;
+  ts.sa = a.sa + m0 * 4;
   ts.b = a.qb + n0 * a.ldb;
-  ts.sb = a.sb + n0 * a.ldsb;
+  ts.sb = a.sb + n0 * 4;
   ts.lda = a.lda;
   ts.ldb = a.ldb;
-  ts.ldsa = a.ldsa;
-  ts.ldsb = a.ldsb;
+  ts.sstep_a = 4 * a.srows_a;
+  ts.sstep_b = 4 * a.srows_b;
+  ts.sbytes_a = steps * ts.sstep_a - m0 * 4;
+  ts.sbytes_b = steps * ts.sstep_b - n0 * 4;
   ts.valid_m = (int)min<int64_t>(kBM, a.M - m0);
   ts.valid_n = (int)min<int64_t>(kBN, a.N - n0);
   ts.k_begin = 0;
-  ts.nk = (int)(a.K / kBK);
+  ts.nk = (int)steps;
   const int esz = a.out_f32 ? 4 : 2;
   ts.out = reinterpret_cast<uint8_t*>(a.out) + (m0 * a.ldo + n0) * esz;
   ts.ldo = a.ldo;
@@ -441,14 +534,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   const int64_t n0 = (int64_t)tn * kBN;
   TileSpec ts;
   const int gb = min(g, a.E - 1);
+  const int64_t steps = a.K / kBK;
   ts.a = a.qa + m0 * a.lda;
-  ts.sa = a.sa + m0 * a.ldsa;
+  ts.sa = a.sa + m0 * 4;
   ts.b = a.qb + gb * a.b_group_stride + n0 * a.ldb;
-  ts.sb = a.sb + gb * a.sb_group_stride + n0 * a.ldsb;
+  ts.sb = a.sb + gb * a.sb_group_stride + n0 * 4;
   ts.lda = a.lda;
   ts.ldb = a.ldb;
-  ts.ldsa = a.ldsa;
-  ts.ldsb = a.ldsb;
+  ts.sstep_a = 4 * a.srows_a;
+  ts.sstep_b = 4 * a.srows_b;
+  ts.sbytes_a = steps * ts.sstep_a - m0 * 4;
+  ts.sbytes_b = steps * ts.sstep_b - n0 * 4;
   ts.valid_m = (int)min<int64_t>(kBM, ends[g] - m0);
   ts.valid_n = (int)min<int64_t>(kBN, a.N - n0);
   ts.k_begin = 0;
@@ -491,14 +587,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_wgrad(GemmArgs a) {
   const int64_t n0 = (int64_t)tn * kBM;   // rows of dW = rows of A (= N)
   const int64_t k0 = (int64_t)tk * kBN;   // cols of dW = rows of B (= K)
   TileSpec ts;
+  const int64_t steps = a.M / kBK;   // 128-token steps of Tcap
   ts.a = a.qa + n0 * a.lda;
-  ts.sa = a.sa + n0 * a.ldsa;
+  ts.sa = a.sa + n0 * 4;
   ts.b = a.qb + k0 * a.ldb;
-  ts.sb = a.sb + k0 * a.ldsb;
+  ts.sb = a.sb + k0 * 4;
   ts.lda = a.lda;
   ts.ldb = a.ldb;
-  ts.ldsa = a.ldsa;
-  ts.ldsb = a.ldsb;
+  ts.sstep_a = 4 * a.srows_a;
+  ts.sstep_b = 4 * a.srows_b;
+  ts.sbytes_a = steps * ts.sstep_a - n0 * 4;
+  ts.sbytes_b = steps * ts.sstep_b - k0 * 4;
   ts.valid_m = (int)min<int64_t>(kBM, a.N - n0);
   ts.valid_n = (int)min<int64_t>(kBN, a.K - k0);
   ts.k_begin = ts0;

@@ -7,17 +7,20 @@
 
 namespace mxk {
 
+// Scale layouts (mx_scale_layout of the C ABI): plain [R, C/32], or k128
+// [C/128, R, 4] (the 4 block scales of a 128-wide step of each row in one
+// dword, rows contiguous per step).
 struct QuantArgs {
   const uint16_t* x;
   int64_t rows, cols, ld;
-  bool rceil;
+  bool rceil, k128;
   uint8_t *q_row, *s_row, *q_col, *s_col;
 };
 
 struct SwigluFwdArgs {
   const uint16_t *a, *b;
   int64_t ld_ab, rows, hidden;
-  bool rceil;
+  bool rceil, k128;
   uint8_t *q_row, *s_row, *q_col, *s_col;
   uint16_t* h_out;
 };
@@ -25,7 +28,7 @@ struct SwigluFwdArgs {
 struct SwigluBwdArgs {
   const uint16_t *dh, *a, *b;
   int64_t ld_dh, ld_ab, rows, hidden;
-  bool rceil;
+  bool rceil, k128;
   uint8_t *q_row, *s_row, *q_col, *s_col;
   uint16_t* dab_out;
 };
@@ -33,16 +36,17 @@ struct SwigluBwdArgs {
 struct DequantArgs {
   const uint8_t *q, *s;
   int64_t rows, cols;
-  bool out_f32;
+  bool out_f32, k128;
   void* out;
 };
 
-// C[m, n] = sum_k A[m, k] B[n, k] over MX operands (see mx_gemm.hip).
+// C[m, n] = sum_k A[m, k] B[n, k] over MX operands (see mx_gemm.hip); the
+// scales are in the k128 layout.
 struct GemmArgs {
   const uint8_t *qa, *sa, *qb, *sb;
   int64_t M, N, K;          // dense: sizes; grouped: M = Tcap
   int64_t lda, ldb;         // code bytes per operand row
-  int64_t ldsa, ldsb;       // scale bytes per operand row
+  int64_t srows_a, srows_b; // rows of each operand's scale matrix (one matrix per expert for B)
   int64_t b_group_stride;   // grouped fwd/dgrad: bytes between experts' B
   int64_t sb_group_stride;  // and between their scales
   int64_t out_group_stride; // wgrad: elements between experts' outputs

@@ -34,11 +34,15 @@ constexpr int kTileChunks = kTR * kTC / 8 / kTileThreads;   // 8 per thread
 struct TileOut {
   uint8_t* q;      // codes
   uint8_t* s;      // scales
-  int64_t ld;      // codes per output row (scale row = ld / 32 bytes)
+  int64_t ld;      // codes per output row (plain scale row = ld / 32 bytes)
+  int64_t srows;   // output rows (the k128 layout's step stride, in dwords)
+  bool k128;       // scales in the k128 layout [ld/128, srows, 4]
 };
 
 // Row-wise quantization of the thread's 8 chunks. The tile's (0,0) sits at
-// row r0, column c0 of the output. All lanes must reach this function.
+// row r0, column c0 of the output. All lanes must reach this function. In the
+// k128 layout (c0 % 128 == 0) a row's four block scales form one dword: the
+// 16 lanes of the row gather it with two lane swaps and one lane stores it.
 __device__ __forceinline__ void tile_rowq(const uint4 (&v)[kTileChunks], int rows_valid,
                                           int cols_valid, bool rceil, TileOut o, int64_t r0,
                                           int64_t c0) {
@@ -50,11 +54,21 @@ __device__ __forceinline__ void tile_rowq(const uint4 (&v)[kTileChunks], int row
     const int row = (t >> 4) + 16 * j;
     const uint32_t sb = scale_byte(quad_max(absmax8_bits(v[j])), rceil);
     const uint2 codes = e4m3_chunk(v[j], inv_scale(sb), sb == 0xFFu);
+    uint32_t packed = 0;
+    if (o.k128) {
+      packed = sb << (8 * (cc >> 2));
+      packed |= (uint32_t)__shfl_xor((int)packed, 4);
+      packed |= (uint32_t)__shfl_xor((int)packed, 8);
+    }
     if (row < rows_valid && colok) {
       const int64_t orow = r0 + row;
       const int64_t ocol = c0 + cc * 8;
       *reinterpret_cast<uint2*>(o.q + orow * o.ld + ocol) = codes;
-      if ((cc & 3) == 0) o.s[orow * (o.ld / kBlock) + ocol / kBlock] = (uint8_t)sb;
+      if (o.k128) {
+        if (cc == 0) *reinterpret_cast<uint32_t*>(o.s + ((c0 >> 7) * o.srows + orow) * 4) = packed;
+      } else if ((cc & 3) == 0) {
+        o.s[orow * (o.ld / kBlock) + ocol / kBlock] = (uint8_t)sb;
+      }
     }
   }
 }
@@ -69,7 +83,8 @@ __device__ __forceinline__ void tile_to_lds(const uint4 (&v)[kTileChunks], uint4
 // Column-wise quantization from the LDS tile: thread t takes columns
 // 2p, 2p+1 (p = t & 63) and rows 32 b .. 32 b + 31 (b = t >> 6) of the tile,
 // i.e. one output block in each of two output rows. Output row = tile
-// column c0 + col, output column = tile row r0 + row.
+// column c0 + col, output column = tile row r0 + row. In the k128 layout
+// (r0 % 128 == 0) block b is byte b of the output row's step dword.
 __device__ __forceinline__ void tile_colq(const uint4* lds4, int rows_valid, int cols_valid,
                                           bool rceil, TileOut o, int64_t r0, int64_t c0) {
   const uint32_t* lds = reinterpret_cast<const uint32_t*>(lds4);
@@ -119,8 +134,14 @@ __device__ __forceinline__ void tile_colq(const uint4* lds4, int rows_valid, int
   d0[1] = make_uint4(c0w[4], c0w[5], c0w[6], c0w[7]);
   d1[0] = make_uint4(c1w[0], c1w[1], c1w[2], c1w[3]);
   d1[1] = make_uint4(c1w[4], c1w[5], c1w[6], c1w[7]);
-  o.s[orow0 * (o.ld / kBlock) + ocol / kBlock] = (uint8_t)sb0;
-  o.s[(orow0 + 1) * (o.ld / kBlock) + ocol / kBlock] = (uint8_t)sb1;
+  if (o.k128) {
+    uint8_t* sd = o.s + ((r0 >> 7) * o.srows + orow0) * 4 + b;
+    sd[0] = (uint8_t)sb0;
+    sd[4] = (uint8_t)sb1;
+  } else {
+    o.s[orow0 * (o.ld / kBlock) + ocol / kBlock] = (uint8_t)sb0;
+    o.s[(orow0 + 1) * (o.ld / kBlock) + ocol / kBlock] = (uint8_t)sb1;
+  }
 }
 
 // Loads the thread's chunks of a bf16 tile whose (0,0) is `base` with row
@@ -162,13 +183,13 @@ __global__ __launch_bounds__(kTileThreads) void k_quant_tile(QuantArgs a) {
   uint4 v[kTileChunks];
   tile_load(v, a.x + (bz * a.rows + r0) * a.ld + c0, a.ld, rows_valid, cols_valid);
   if (a.q_row) {
-    TileOut o{a.q_row + bz * a.rows * a.cols, a.s_row + bz * a.rows * (a.cols / kBlock), a.cols};
+    TileOut o{a.q_row + bz * a.rows * a.cols, a.s_row + bz * a.rows * (a.cols / kBlock), a.cols, a.rows, a.k128};
     tile_rowq(v, rows_valid, cols_valid, a.rceil, o, r0, c0);
   }
   if (a.q_col) {
     tile_to_lds(v, lds);
     __syncthreads();
-    TileOut o{a.q_col + bz * a.rows * a.cols, a.s_col + bz * a.cols * (a.rows / kBlock), a.rows};
+    TileOut o{a.q_col + bz * a.rows * a.cols, a.s_col + bz * a.cols * (a.rows / kBlock), a.rows, a.cols, a.k128};
     tile_colq(lds, rows_valid, cols_valid, a.rceil, o, r0, c0);
   }
 }
@@ -199,10 +220,10 @@ __global__ __launch_bounds__(kTileThreads) void k_swiglu_fwd(SwigluFwdArgs a) {
     v[j] = make_uint4(swiglu_pair(v[j].x, w[j].x), swiglu_pair(v[j].y, w[j].y),
                       swiglu_pair(v[j].z, w[j].z), swiglu_pair(v[j].w, w[j].w));
   if (a.h_out) tile_store_bf16(v, a.h_out + r0 * a.hidden + c0, a.hidden, rows_valid, cols_valid);
-  tile_rowq(v, rows_valid, cols_valid, a.rceil, TileOut{a.q_row, a.s_row, a.hidden}, r0, c0);
+  tile_rowq(v, rows_valid, cols_valid, a.rceil, TileOut{a.q_row, a.s_row, a.hidden, a.rows, a.k128}, r0, c0);
   tile_to_lds(v, lds);
   __syncthreads();
-  tile_colq(lds, rows_valid, cols_valid, a.rceil, TileOut{a.q_col, a.s_col, a.rows}, r0, c0);
+  tile_colq(lds, rows_valid, cols_valid, a.rceil, TileOut{a.q_col, a.s_col, a.rows, a.hidden, a.k128}, r0, c0);
 }
 
 // dA = dh*b*s*(1 + a*(1-s)), dB = dh*a*s with s = sigmoid(a), float32.
@@ -250,10 +271,10 @@ __global__ __launch_bounds__(kTileThreads) void k_swiglu_bwd(SwigluBwdArgs a) {
     tile_store_bf16(da, a.dab_out + r0 * H2 + c0, H2, rows_valid, cols_valid);
     tile_store_bf16(db, a.dab_out + r0 * H2 + a.hidden + c0, H2, rows_valid, cols_valid);
   }
-  const TileOut orow{a.q_row, a.s_row, H2};
+  const TileOut orow{a.q_row, a.s_row, H2, a.rows, a.k128};
   tile_rowq(da, rows_valid, cols_valid, a.rceil, orow, r0, c0);
   tile_rowq(db, rows_valid, cols_valid, a.rceil, orow, r0, a.hidden + c0);
-  const TileOut ocol{a.q_col, a.s_col, a.rows};
+  const TileOut ocol{a.q_col, a.s_col, a.rows, H2, a.k128};
   tile_to_lds(da, lds);
   __syncthreads();
   tile_colq(lds, rows_valid, cols_valid, a.rceil, ocol, r0, c0);
@@ -271,7 +292,13 @@ __global__ __launch_bounds__(256) void k_dequant(DequantArgs a) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
     const uint4 c = *reinterpret_cast<const uint4*>(a.q + 16 * i);
-    const uint32_t sb = a.s[i >> 1];
+    uint32_t sb;
+    if (a.k128) {
+      const int64_t r = (16 * i) / a.cols, blk = ((16 * i) % a.cols) >> 5;
+      sb = a.s[((blk >> 2) * a.rows + r) * 4 + (blk & 3)];
+    } else {
+      sb = a.s[i >> 1];
+    }
     uint32_t w[4] = {c.x, c.y, c.z, c.w};
     float f[16];
 #pragma unroll

@@ -49,10 +49,10 @@ def _q_out(lead, R, C, dev, row=True, col=True):
     o = {}
     if row:
         o["q_row"] = torch.empty(lead + (R, C), dtype=torch.uint8, device=dev)
-        o["s_row"] = torch.empty(lead + (R, C // 32), dtype=torch.uint8, device=dev)
+        o["s_row"] = torch.empty(lead + mx.scale_shape(R, C), dtype=torch.uint8, device=dev)
     if col:
         o["q_col"] = torch.empty(lead + (C, R), dtype=torch.uint8, device=dev)
-        o["s_col"] = torch.empty(lead + (C, R // 32), dtype=torch.uint8, device=dev)
+        o["s_col"] = torch.empty(lead + mx.scale_shape(C, R), dtype=torch.uint8, device=dev)
     return o
 
 

@@ -18,7 +18,9 @@ LIB_PATH = os.path.join(_HERE, "libmxfp8.so")
 RCEIL, FLOOR = 0, 1
 BF16, F32 = 0, 1
 ROWWISE, COLWISE = 1, 2
+SCALES_PLAIN, SCALES_K128 = 0, 1
 _MODES = {"rceil": RCEIL, "floor": FLOOR, RCEIL: RCEIL, FLOOR: FLOOR}
+_LAYOUTS = {"plain": SCALES_PLAIN, "k128": SCALES_K128}
 _DT = {torch.bfloat16: BF16, torch.float32: F32, "bf16": BF16, "f32": F32}
 
 _lib = None
@@ -30,11 +32,13 @@ _SIGS = {
     "mx_abi_version": ([], ctypes.c_int),
     "mx_last_error": ([], ctypes.c_char_p),
     "mx_init": ([], ctypes.c_int),
-    "mx_quantize": ([_P, _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_uint, _P, _P, _P, _P, _P], ctypes.c_int),
-    "mx_dequantize": ([_P, _P, _I64, _I64, ctypes.c_int, _P, _P], ctypes.c_int),
-    "mx_swiglu_quant_fwd": ([_P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _P, _P, _P], ctypes.c_int),
-    "mx_swiglu_quant_bwd": ([_P, _I64, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _P, _P, _P],
+    "mx_quantize": ([_P, _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_uint, ctypes.c_int, _P, _P, _P, _P, _P],
+                    ctypes.c_int),
+    "mx_dequantize": ([_P, _P, _I64, _I64, ctypes.c_int, ctypes.c_int, _P, _P], ctypes.c_int),
+    "mx_swiglu_quant_fwd": ([_P, _P, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int, _P, _P, _P, _P, _P, _P],
                             ctypes.c_int),
+    "mx_swiglu_quant_bwd": ([_P, _I64, _P, _P, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int, _P, _P, _P, _P, _P,
+                             _P], ctypes.c_int),
     "mx_scaled_mm": ([_P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _I64, _P], ctypes.c_int),
     "mx_scaled_grouped_mm_fwd": ([_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P],
                                  ctypes.c_int),
@@ -85,11 +89,17 @@ def _u8(shape, device):
     return torch.empty(shape, dtype=torch.uint8, device=device)
 
 
-def quantize(x, mode="rceil", rowwise=True, colwise=False, out=None):
+def scale_shape(R, C, layout="k128"):
+    """Shape of the scale tensor of an [R, C] code matrix: plain [R, C/32],
+    k128 [C/128, R, 4]."""
+    return (C // 128, R, 4) if layout == "k128" else (R, C // 32)
+
+
+def quantize(x, mode="rceil", rowwise=True, colwise=False, layout="k128", out=None):
     """MX-quantize bf16 x [..., R, C] (row stride may exceed C).
 
-    Returns dict with q_row [..., R, C], s_row [..., R, C/32] and/or
-    q_col [..., C, R], s_col [..., C, R/32] (uint8)."""
+    Returns dict with q_row [..., R, C] and s_row (the scales of that [R, C]
+    matrix, see scale_shape) and/or q_col [..., C, R] and s_col (uint8)."""
     assert x.dtype == torch.bfloat16 and x.stride(-1) == 1
     R, C = x.shape[-2], x.shape[-1]
     lead = tuple(x.shape[:-2])
@@ -104,28 +114,31 @@ def quantize(x, mode="rceil", rowwise=True, colwise=False, out=None):
     dev = x.device
     if rowwise:
         out.setdefault("q_row", _u8(lead + (R, C), dev))
-        out.setdefault("s_row", _u8(lead + (R, C // 32), dev))
+        out.setdefault("s_row", _u8(lead + scale_shape(R, C, layout), dev))
     if colwise:
         out.setdefault("q_col", _u8(lead + (C, R), dev))
-        out.setdefault("s_col", _u8(lead + (C, R // 32), dev))
+        out.setdefault("s_col", _u8(lead + scale_shape(C, R, layout), dev))
     dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
-    st = lib().mx_quantize(_ptr(x), batch, R, C, ld, _MODES[mode], dirs,
+    st = lib().mx_quantize(_ptr(x), batch, R, C, ld, _MODES[mode], dirs, _LAYOUTS[layout],
                            _ptr(out.get("q_row")), _ptr(out.get("s_row")),
                            _ptr(out.get("q_col")), _ptr(out.get("s_col")), _stream(dev))
     _check(st, "mx_quantize")
     return out
 
 
-def dequantize(q, s, out_dtype=torch.float32, out=None):
+def dequantize(q, s, out_dtype=torch.float32, layout=None, out=None):
+    """layout defaults to k128 for a 3-D scale tensor, plain for 2-D."""
     R, C = q.shape
+    if layout is None:
+        layout = "k128" if s.dim() == 3 else "plain"
     if out is None:
         out = torch.empty((R, C), dtype=out_dtype, device=q.device)
-    _check(lib().mx_dequantize(_ptr(q), _ptr(s), R, C, _DT[out.dtype], _ptr(out), _stream(q.device)),
-           "mx_dequantize")
+    _check(lib().mx_dequantize(_ptr(q), _ptr(s), R, C, _LAYOUTS[layout], _DT[out.dtype], _ptr(out),
+                               _stream(q.device)), "mx_dequantize")
     return out
 
 
-def swiglu_quant_fwd(a, b, mode="rceil", want_h=False, out=None):
+def swiglu_quant_fwd(a, b, mode="rceil", want_h=False, layout="k128", out=None):
     """Fused SwiGLU + dual quantization. a, b: bf16 [T, H] views sharing a row
     stride (e.g. the two halves of the w13 output)."""
     assert a.stride(0) == b.stride(0) and a.stride(1) == 1 and b.stride(1) == 1
@@ -133,31 +146,31 @@ def swiglu_quant_fwd(a, b, mode="rceil", want_h=False, out=None):
     dev = a.device
     out = dict(out or {})
     out.setdefault("q_row", _u8((T, H), dev))
-    out.setdefault("s_row", _u8((T, H // 32), dev))
+    out.setdefault("s_row", _u8(scale_shape(T, H, layout), dev))
     out.setdefault("q_col", _u8((H, T), dev))
-    out.setdefault("s_col", _u8((H, T // 32), dev))
+    out.setdefault("s_col", _u8(scale_shape(H, T, layout), dev))
     if want_h:
         out.setdefault("h", torch.empty((T, H), dtype=torch.bfloat16, device=dev))
-    st = lib().mx_swiglu_quant_fwd(_ptr(a), _ptr(b), a.stride(0), T, H, _MODES[mode],
+    st = lib().mx_swiglu_quant_fwd(_ptr(a), _ptr(b), a.stride(0), T, H, _MODES[mode], _LAYOUTS[layout],
                                    _ptr(out["q_row"]), _ptr(out["s_row"]), _ptr(out["q_col"]),
                                    _ptr(out["s_col"]), _ptr(out.get("h")), _stream(dev))
     _check(st, "mx_swiglu_quant_fwd")
     return out
 
 
-def swiglu_quant_bwd(dh, a, b, mode="rceil", want_dab=False, out=None):
+def swiglu_quant_bwd(dh, a, b, mode="rceil", want_dab=False, layout="k128", out=None):
     assert a.stride(0) == b.stride(0) and dh.stride(1) == 1
     T, H = a.shape
     dev = a.device
     out = dict(out or {})
     out.setdefault("q_row", _u8((T, 2 * H), dev))
-    out.setdefault("s_row", _u8((T, 2 * H // 32), dev))
+    out.setdefault("s_row", _u8(scale_shape(T, 2 * H, layout), dev))
     out.setdefault("q_col", _u8((2 * H, T), dev))
-    out.setdefault("s_col", _u8((2 * H, T // 32), dev))
+    out.setdefault("s_col", _u8(scale_shape(2 * H, T, layout), dev))
     if want_dab:
         out.setdefault("dab", torch.empty((T, 2 * H), dtype=torch.bfloat16, device=dev))
     st = lib().mx_swiglu_quant_bwd(_ptr(dh), dh.stride(0), _ptr(a), _ptr(b), a.stride(0), T, H,
-                                   _MODES[mode], _ptr(out["q_row"]), _ptr(out["s_row"]),
+                                   _MODES[mode], _LAYOUTS[layout], _ptr(out["q_row"]), _ptr(out["s_row"]),
                                    _ptr(out["q_col"]), _ptr(out["s_col"]), _ptr(out.get("dab")),
                                    _stream(dev))
     _check(st, "mx_swiglu_quant_bwd")
@@ -165,6 +178,7 @@ def swiglu_quant_bwd(dh, a, b, mode="rceil", want_dab=False, out=None):
 
 
 def scaled_mm(qa, sa, qb, sb, out_dtype=torch.bfloat16, out=None):
+    """GEMM of two MX operands with k128 scales."""
     M, K = qa.shape
     N = qb.shape[0]
     if out is None:

@@ -72,6 +72,29 @@ def real_mx(shape, std, seed, mode="rceil", colwise=False):
     return q["q_" + k], q["s_" + k], b
 
 
+def k128(s):
+    """Plain scales [..., R, C/32] -> the library's k128 layout
+    [..., C/128, R, 4] (a pure permutation, byte ((j/4) R + r) 4 + j%4)."""
+    s = np.asarray(s)
+    R, nb = s.shape[-2], s.shape[-1]
+    assert nb % 4 == 0
+    t = s.reshape(s.shape[:-1] + (nb // 4, 4))
+    return np.ascontiguousarray(np.moveaxis(t, -3, -2))
+
+
+def plain(s):
+    """Inverse of k128: [..., C/128, R, 4] -> [..., R, C/32]."""
+    s = np.asarray(s)
+    t = np.moveaxis(s, -3, -2)
+    return np.ascontiguousarray(t.reshape(t.shape[:-2] + (t.shape[-2] * 4,)))
+
+
+def host_plain(t):
+    """Device scale tensor (k128 if 3-D per matrix, else plain) -> plain numpy."""
+    a = host(t)
+    return plain(a) if a.ndim >= 3 and a.shape[-1] == 4 else a
+
+
 def frob_rel(got, ref):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)

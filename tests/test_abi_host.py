@@ -34,20 +34,29 @@ def test_header_symbols_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
     assert sorted(mx.EXPORTS) == names
-    assert L.mx_abi_version() == 1
+    assert L.mx_abi_version() == 2
 
 
 def test_argument_errors_are_reported_without_device_work():
     L = _lib()
     p = ctypes.c_void_p(16)   # never dereferenced: validation fails first
     # cols not a multiple of 32
-    st = L.mx_quantize(p, 1, 64, 48, 48, 0, 1, p, p, None, None, None)
+    st = L.mx_quantize(p, 1, 64, 48, 48, 0, 1, 0, p, p, None, None, None)
     assert st == 2 and b"multiple of 32" in L.mx_last_error()
-    # bad scale mode / direction bits
-    assert L.mx_quantize(p, 1, 64, 64, 64, 7, 1, p, p, None, None, None) == 4
-    assert L.mx_quantize(p, 1, 64, 64, 64, 0, 8, p, p, None, None, None) == 4
-    # misaligned pointer
-    assert L.mx_quantize(ctypes.c_void_p(18), 1, 64, 64, 64, 0, 1, p, p, None, None, None) == 3
+    # K128 scales need the block axis to be a multiple of 128 (row-wise: cols;
+    # column-wise: rows)
+    st = L.mx_quantize(p, 1, 128, 96, 96, 0, 1, 1, p, p, None, None, None)
+    assert st == 2 and b"multiple of 128" in L.mx_last_error()
+    assert L.mx_quantize(p, 1, 96, 128, 128, 0, 2, 1, None, None, p, p, None) == 2
+    # bad scale mode / direction bits / layout
+    assert L.mx_quantize(p, 1, 64, 64, 64, 7, 1, 0, p, p, None, None, None) == 4
+    assert L.mx_quantize(p, 1, 64, 64, 64, 0, 8, 0, p, p, None, None, None) == 4
+    assert L.mx_quantize(p, 1, 64, 64, 64, 0, 1, 2, p, p, None, None, None) == 4
+    # misaligned pointer; K128 scales must be 4-byte aligned
+    assert L.mx_quantize(ctypes.c_void_p(18), 1, 64, 64, 64, 0, 1, 0, p, p, None, None, None) == 3
+    assert L.mx_quantize(p, 1, 128, 128, 128, 0, 1, 1, p, ctypes.c_void_p(18), None, None, None) == 3
+    assert L.mx_dequantize(p, p, 32, 96, 1, 0, p, None) == 2
+    assert L.mx_swiglu_quant_fwd(p, p, 192, 64, 96, 0, 1, p, p, p, p, None, None) == 2
     # K not a multiple of 128
     assert L.mx_scaled_mm(p, p, p, p, 32, 32, 96, 0, p, 32, None) == 2
     # grouped: Tcap not a multiple of 128, bad E
@@ -63,6 +72,25 @@ def test_valid_call_without_gpu_fails_loudly():
         pytest.skip("a GPU is present; the device path is covered by the gpu tests")
     L = _lib()
     p = ctypes.c_void_p(16)
-    st = L.mx_quantize(p, 1, 64, 64, 64, 0, 1, p, p, None, None, None)
+    st = L.mx_quantize(p, 1, 64, 64, 64, 0, 1, 0, p, p, None, None, None)
     assert st == 5
     assert L.mx_last_error()
+
+
+def test_k128_scale_layout_permutation():
+    """The tests' layout converters follow the header's K128 formula: byte
+    ((j/4) * R + r) * 4 + j%4 holds the scale of row r, block j."""
+    import numpy as np
+
+    from _helpers import k128, plain
+    rng = np.random.default_rng(0)
+    for lead, R, nb in (((), 5, 8), ((3,), 7, 4), ((2, 2), 3, 12)):
+        s = rng.integers(0, 256, lead + (R, nb)).astype(np.uint8)
+        t = k128(s)
+        assert t.shape == lead + (nb // 4, R, 4)
+        flat = t.reshape(lead + (-1,))
+        for idx in np.ndindex(*lead):
+            for r in range(R):
+                for j in range(nb):
+                    assert flat[idx + (((j // 4) * R + r) * 4 + j % 4,)] == s[idx + (r, j)]
+        np.testing.assert_array_equal(plain(t), s)

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from _helpers import (FROB_MFMA, bf16_host, bf16_ulp_check, dev, frob_rel, host, mfma_bound, rand_mx,
+from _helpers import (FROB_MFMA, bf16_host, bf16_ulp_check, dev, frob_rel, host, k128, mfma_bound, rand_mx,
                       real_mx, to_dev)
 from oracle import mx as O
 from quantize_grouped_gemm_amd import mx, synth
@@ -19,7 +19,8 @@ pytestmark = pytest.mark.gpu
 
 
 def _mx_dev(q, s):
-    return to_dev(q), to_dev(s)
+    """Oracle operand (plain scales) -> device codes and k128 scales."""
+    return to_dev(q), to_dev(k128(s))
 
 
 def _check(got, A, B, ref, out_dtype, what="", frob=FROB_MFMA):
@@ -197,8 +198,9 @@ def test_invalid_offsets_flag_dev_err(gpu):
 
 def test_abi_rejects_bad_arguments(gpu):
     qa, sa = rand_mx((128, 96), 1)
+    q, s = to_dev(qa), to_dev(sa)
     with pytest.raises(mx.MXError):
-        mx.scaled_mm(*_mx_dev(qa, sa), *_mx_dev(qa, sa))          # K = 96 not a multiple of 128
+        mx.scaled_mm(q, s, q, s)                                  # K = 96 not a multiple of 128
     with pytest.raises(mx.MXError):
         mx.quantize(torch.zeros((64, 48), dtype=torch.bfloat16, device=dev()))   # cols % 32
 

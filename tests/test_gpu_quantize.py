@@ -1,13 +1,14 @@
 """GPU parity of MX quantization and dequantization against the oracle:
-bit-exact codes and scales, every direction and mode, ragged tiles, batches,
-strided rows, every finite bf16 value, the stress tensor's planted cases, and
-sampled blocks of the full [32768, 7168] stress tensor."""
+bit-exact codes and scales (in both scale layouts; k128 scales are compared
+after the inverse permutation), every direction and mode, ragged tiles,
+batches, strided rows, every finite bf16 value, the stress tensor's planted
+cases, and sampled blocks of the full [32768, 7168] stress tensor."""
 
 import numpy as np
 import pytest
 import torch
 
-from _helpers import bf16_host, dev, host, to_dev
+from _helpers import bf16_host, dev, host, k128, plain, to_dev
 from oracle import mx as O
 from quantize_grouped_gemm_amd import mx, synth
 
@@ -16,11 +17,15 @@ pytestmark = pytest.mark.gpu
 MODES = ["rceil", "floor"]
 
 
-def _check_quant(xb_host, xt, mode, rowwise=True, colwise=True):
-    got = mx.quantize(xt, mode, rowwise, colwise)
+def _check_quant(xb_host, xt, mode, rowwise=True, colwise=True, layout="k128"):
+    got = mx.quantize(xt, mode, rowwise, colwise, layout=layout)
     ref = O.quantize_bf16(xb_host, mode, rowwise, colwise)
     for k in ref:
-        np.testing.assert_array_equal(host(got[k]), ref[k], err_msg=f"{k} {mode}")
+        g = host(got[k])
+        if k.startswith("s_") and layout == "k128":
+            assert g.shape[-1] == 4 and g.shape[-2] == ref[k].shape[-2]
+            g = plain(g)
+        np.testing.assert_array_equal(g, ref[k], err_msg=f"{k} {mode} {layout}")
     return got
 
 
@@ -28,27 +33,44 @@ def _check_quant(xb_host, xt, mode, rowwise=True, colwise=True):
 @pytest.mark.parametrize("shape", [(32, 32), (64, 96), (160, 224), (256, 512), (384, 128)])
 def test_quantize_shapes(gpu, mode, shape):
     xb = synth.bits(synth.stress_tensor(*shape, seed=sum(shape)))
-    _check_quant(xb, to_dev(xb.view(np.int16)).view(torch.bfloat16), mode)
+    _check_quant(xb, to_dev(xb.view(np.int16)).view(torch.bfloat16), mode, layout="plain")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", [(128, 128), (256, 512), (384, 128), (640, 384)])
+def test_quantize_shapes_k128(gpu, mode, shape):
+    xb = synth.bits(synth.stress_tensor(*shape, seed=sum(shape) + 1))
+    _check_quant(xb, to_dev(xb.view(np.int16)).view(torch.bfloat16), mode, layout="k128")
 
 
 @pytest.mark.parametrize("mode", MODES)
 def test_quantize_rowwise_any_rows_and_separate_directions(gpu, mode):
     xb = synth.bits(synth.normal_bf16((100, 96), 1.0, synth.generator(3)))
     xt = to_dev(xb.view(np.int16)).view(torch.bfloat16)
-    _check_quant(xb, xt, mode, True, False)
+    _check_quant(xb, xt, mode, True, False, layout="plain")
     xb = xb[:96]
     xt = xt[:96].contiguous()
-    _check_quant(xb, xt, mode, False, True)
+    _check_quant(xb, xt, mode, False, True, layout="plain")
+    # k128: row-wise takes any row count; column-wise needs rows % 128
+    xb = synth.bits(synth.normal_bf16((100, 256), 1.0, synth.generator(4)))
+    _check_quant(xb, to_dev(xb.view(np.int16)).view(torch.bfloat16), mode, True, False)
+    xb = synth.bits(synth.normal_bf16((256, 96), 1.0, synth.generator(5)))
+    _check_quant(xb, to_dev(xb.view(np.int16)).view(torch.bfloat16), mode, False, True)
 
 
 @pytest.mark.parametrize("mode", MODES)
 def test_quantize_batched_and_strided(gpu, mode):
     xb = synth.bits(synth.stress_tensor(3 * 64, 96, seed=11)).reshape(3, 64, 96)
+    _check_quant(xb, to_dev(xb.view(np.int16)).view(torch.bfloat16), mode, layout="plain")
+    xb = synth.bits(synth.stress_tensor(3 * 128, 256, seed=13)).reshape(3, 128, 256)
     _check_quant(xb, to_dev(xb.view(np.int16)).view(torch.bfloat16), mode)
     # rows with a leading dimension larger than the width (a column slice)
     wide = synth.bits(synth.stress_tensor(128, 320, seed=12))
     wt = to_dev(wide.view(np.int16)).view(torch.bfloat16)
-    _check_quant(wide[:, 64:256], wt[:, 64:256], mode)
+    _check_quant(wide[:, 64:256], wt[:, 64:256], mode, layout="plain")
+    wide = synth.bits(synth.stress_tensor(256, 640, seed=14))
+    wt = to_dev(wide.view(np.int16)).view(torch.bfloat16)
+    _check_quant(wide[:, 128:384], wt[:, 128:384], mode)
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -76,7 +98,12 @@ def test_quantize_nonfinite_blocks(gpu):
     xb[40, 33] = 0xFF80   # -inf
     xb[10, 62] = 0x7F80   # +inf
     for mode in MODES:
-        _check_quant(xb, to_dev(xb.view(np.int16)).view(torch.bfloat16), mode)
+        _check_quant(xb, to_dev(xb.view(np.int16)).view(torch.bfloat16), mode, layout="plain")
+    big = synth.bits(synth.normal_bf16((128, 256), 1.0, synth.generator(10)))
+    big[3, 5] = 0x7FC0
+    big[100, 200] = 0xFF80
+    for mode in MODES:
+        _check_quant(big, to_dev(big.view(np.int16)).view(torch.bfloat16), mode)
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -98,24 +125,29 @@ def test_stress_full_size_sampled(gpu, mode):
     assert len(special_rows) >= 64 and len(special_cols) >= 64
     ri = torch.as_tensor(rows, device=dev())
     ci = torch.as_tensor(cols, device=dev())
+    s_row = plain(host(got["s_row"]))
+    s_col = plain(host(got["s_col"]))
     q, s = O.quantize(O.bf16_to_f64(bf16_host(x[ri])), mode)
     np.testing.assert_array_equal(host(got["q_row"][ri]), q)
-    np.testing.assert_array_equal(host(got["s_row"][ri]), s)
+    np.testing.assert_array_equal(s_row[rows], s)
     q, s = O.quantize(O.bf16_to_f64(bf16_host(x[:, ci])).T, mode)
     np.testing.assert_array_equal(host(got["q_col"][ci]), q)
-    np.testing.assert_array_equal(host(got["s_col"][ci]), s)
+    np.testing.assert_array_equal(s_col[cols], s)
     # dequantize round trip on the same rows: bit-exact against the oracle
     deq = mx.dequantize(got["q_row"], got["s_row"], torch.float32)
-    ref = O.f64_to_f32(O.dequantize(host(got["q_row"][ri]), host(got["s_row"][ri])))
+    ref = O.f64_to_f32(O.dequantize(host(got["q_row"][ri]), s_row[rows]))
     np.testing.assert_array_equal(host(deq[ri]).view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("layout", ["plain", "k128"])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_dequantize_all_codes_all_scales(gpu, out_dtype):
-    """Every code under every scale byte (0..254 and the NaN scale 0xFF)."""
+def test_dequantize_all_codes_all_scales(gpu, out_dtype, layout):
+    """Every code under every scale byte (0..254 and the NaN scale 0xFF); the
+    scale bytes also vary along each row so the layouts differ."""
     codes = np.tile(np.arange(256, dtype=np.uint8), 256 * 4).reshape(256, 1024)   # [scale byte, ...]
-    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 32, axis=1)
-    got = mx.dequantize(to_dev(codes), to_dev(scales), out_dtype)
+    scales = ((np.arange(256)[:, None] + 37 * np.arange(32)[None, :]) % 256).astype(np.uint8)
+    s_dev = to_dev(k128(scales) if layout == "k128" else scales)
+    got = mx.dequantize(to_dev(codes), s_dev, out_dtype, layout=layout)
     ref = O.dequantize(codes, scales)
     if out_dtype == torch.float32:
         g = host(got).astype(np.float64)

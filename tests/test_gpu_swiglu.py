@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 import torch
 
-from _helpers import bf16_host, code_tolerance, dev, host, to_dev
+from _helpers import bf16_host, code_tolerance, dev, host, plain, to_dev
 from oracle import mx as O
 from quantize_grouped_gemm_amd import mx, synth
 
@@ -25,6 +25,13 @@ def _dev_bf16(b):
     return to_dev(b.view(np.int16)).view(torch.bfloat16)
 
 
+def _scales(t, layout):
+    return plain(host(t)) if layout == "k128" else host(t)
+
+
+SHAPES = [(64, 96, "plain"), (160, 224, "plain"), (256, 384, "k128"), (2048, 2048, "k128")]
+
+
 def _assert_close_codes(got, ref, what, frac=1e-5):
     ndiff, nbeyond, n, nscale = code_tolerance(got[0], got[1], ref[0], ref[1])
     assert nbeyond == 0, f"{what}: {nbeyond} elements beyond one E4M3 code"
@@ -32,14 +39,14 @@ def _assert_close_codes(got, ref, what, frac=1e-5):
 
 
 @pytest.mark.parametrize("mode", ["rceil", "floor"])
-@pytest.mark.parametrize("T,H", [(64, 96), (160, 224), (2048, 2048)])
-def test_swiglu_fwd(gpu, mode, T, H):
+@pytest.mark.parametrize("T,H,layout", SHAPES)
+def test_swiglu_fwd(gpu, mode, T, H, layout):
     zb, _ = _inputs(T, H, seed=T + H)
     z = _dev_bf16(zb)
-    got = mx.swiglu_quant_fwd(z[:, :H], z[:, H:], mode, want_h=True)
+    got = mx.swiglu_quant_fwd(z[:, :H], z[:, H:], mode, want_h=True, layout=layout)
     ref = O.swiglu_quant_fwd(zb[:, :H], zb[:, H:], mode)
-    _assert_close_codes((host(got["q_row"]), host(got["s_row"])), (ref["q_row"], ref["s_row"]), "row")
-    _assert_close_codes((host(got["q_col"]), host(got["s_col"])), (ref["q_col"], ref["s_col"]), "col")
+    _assert_close_codes((host(got["q_row"]), _scales(got["s_row"], layout)), (ref["q_row"], ref["s_row"]), "row")
+    _assert_close_codes((host(got["q_col"]), _scales(got["s_col"], layout)), (ref["q_col"], ref["s_col"]), "col")
     # the materialized bf16 h: within one bf16 ulp of the correctly rounded value
     hg = O.bf16_to_f64(bf16_host(got["h"]))
     hr = O.bf16_to_f64(ref["h"])
@@ -47,26 +54,26 @@ def test_swiglu_fwd(gpu, mode, T, H):
     assert np.all(np.abs(hg - hr) <= ulp)
     assert np.mean(hg != hr) < 1e-3
     # fused vs standalone: quantizing the kernel's own bf16 h gives the same bytes
-    st = mx.quantize(got["h"], mode, True, True)
+    st = mx.quantize(got["h"], mode, True, True, layout=layout)
     for k in ("q_row", "s_row", "q_col", "s_col"):
         assert torch.equal(st[k], got[k]), k
 
 
 @pytest.mark.parametrize("mode", ["rceil", "floor"])
-@pytest.mark.parametrize("T,H", [(64, 96), (160, 224), (2048, 2048)])
-def test_swiglu_bwd(gpu, mode, T, H):
+@pytest.mark.parametrize("T,H,layout", SHAPES)
+def test_swiglu_bwd(gpu, mode, T, H, layout):
     zb, dhb = _inputs(T, H, seed=3 * T + H)
     z = _dev_bf16(zb)
     dh = _dev_bf16(dhb)
-    got = mx.swiglu_quant_bwd(dh, z[:, :H], z[:, H:], mode, want_dab=True)
+    got = mx.swiglu_quant_bwd(dh, z[:, :H], z[:, H:], mode, want_dab=True, layout=layout)
     ref = O.swiglu_quant_bwd(dhb, zb[:, :H], zb[:, H:], mode)
-    _assert_close_codes((host(got["q_row"]), host(got["s_row"])), (ref["q_row"], ref["s_row"]), "row")
-    _assert_close_codes((host(got["q_col"]), host(got["s_col"])), (ref["q_col"], ref["s_col"]), "col")
+    _assert_close_codes((host(got["q_row"]), _scales(got["s_row"], layout)), (ref["q_row"], ref["s_row"]), "row")
+    _assert_close_codes((host(got["q_col"]), _scales(got["s_col"], layout)), (ref["q_col"], ref["s_col"]), "col")
     dg = O.bf16_to_f64(bf16_host(got["dab"]))
     dr = O.bf16_to_f64(ref["dab"])
     ulp = np.exp2(np.maximum(np.floor(np.log2(np.where(dr != 0, np.abs(dr), 1.0))), -126) - 7)
     assert np.all(np.abs(dg - dr) <= ulp)
-    st = mx.quantize(got["dab"], mode, True, True)
+    st = mx.quantize(got["dab"], mode, True, True, layout=layout)
     for k in ("q_row", "s_row", "q_col", "s_col"):
         assert torch.equal(st[k], got[k]), k
 
@@ -80,7 +87,7 @@ def test_swiglu_special_values(gpu):
     zb[8:16, 32:H] = 0xC47A                         # a = -1000
     zb[16:24, 32:H] = 0x447A                        # a = +1000
     z = _dev_bf16(zb)
-    got = mx.swiglu_quant_fwd(z[:, :H], z[:, H:], "rceil", want_h=True)
+    got = mx.swiglu_quant_fwd(z[:, :H], z[:, H:], "rceil", want_h=True, layout="plain")
     ref = O.swiglu_quant_fwd(zb[:, :H], zb[:, H:], "rceil")
     np.testing.assert_array_equal(bf16_host(got["h"]) & 0x7FFF, ref["h"] & 0x7FFF)
     for k in ("q_row", "s_row", "q_col", "s_col"):
