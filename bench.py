@@ -35,6 +35,38 @@ PEAK_HBM = 8.0e12        # HBM3E bytes/s
 
 WORKLOADS = ("moe_scout", "moe_dsv3", "moe_dsv3_hp", "dense", "quant", "linear", "copy")
 
+# HBM traffic of the dominant kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# passes scaled by a 1 GiB copy (see the file); used only while the kernel's
+# sources are the ones the counters were taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_grouped_moe_scout_traffic.md")
+GEMM_SOURCES = ("quantize_grouped_gemm_amd/csrc/mx_gemm.hip", "quantize_grouped_gemm_amd/csrc/mx_kernels.h",
+                "quantize_grouped_gemm_amd/csrc/mx_device.h", "quantize_grouped_gemm_amd/build.py")
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _measured_traffic():
+    """Bytes per launch of k_gemm_grouped on the default workload, or None if
+    the counters were taken on other kernel sources."""
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith(("#", " ", "|", "-")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("source_sha256") != gemm_source_hash():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
 
 def _args():
     ap = argparse.ArgumentParser()
@@ -139,12 +171,15 @@ def _kernel_table(stages, per):
     return out, table
 
 
-def _roofline_gemm(table, kernel, peak):
+def _roofline_gemm(table, kernel, peak, traffic=None):
     e = table[kernel]
     achieved = e["flops"] / e["seconds"]       # per-launch flops / per-launch time, averaged
-    return {"kernel": kernel, "bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": peak / 1e12,
-            "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-            "per_launch_flops": e["flops"] / e["launches"], "avg_launch_us": round(e["seconds"] / e["launches"] * 1e6, 2)}
+    r = {"kernel": kernel, "bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": peak / 1e12,
+         "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+         "per_launch_flops": e["flops"] / e["launches"], "avg_launch_us": round(e["seconds"] / e["launches"] * 1e6, 2)}
+    if traffic is not None:
+        r["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)"
+    return r
 
 
 def _quant_component(torch, dev, reps=10):
@@ -279,7 +314,8 @@ def main():
         "dtype": "mxfp8",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, routed group sizes)",
         "config": config,
-        "roofline": _roofline_gemm(table, gemm_kernel, PEAK_MXFP8),
+        "roofline": _roofline_gemm(table, gemm_kernel, PEAK_MXFP8,
+                                   _measured_traffic() if name == "moe_scout" else None),
         "step_roofline": {"gemm_useful_tflops": round(gemm_flops / gemm_time / 1e12, 1),
                           "ideal_ms": round(roof_time * 1e3, 4), "frac": round(roof_time / wall, 4)},
         "kernels": kernels,
