@@ -74,6 +74,8 @@ struct TileSpec {
   int valid_m, valid_n;  // A rows / B rows that exist in this tile (1..256)
   int64_t k_begin;       // first contraction index, multiple of 128
   int nk;                // number of 128-wide K steps (0 => C = 0)
+  int pf_a0, pf_an;      // rows [pf_a0, pf_a0 + pf_an) of A and
+  int pf_b0, pf_bn;      // rows [pf_b0, pf_b0 + pf_bn) of B are this tile's L2 prefetch share
   void* out;             // C(0, 0) of the tile
   int64_t ldo;
   bool out_f32;
@@ -206,7 +208,7 @@ __device__ __forceinline__ void wg_barrier() {
 struct TileDma {
   __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
   uint32_t voff_a[2], voff_b[2];
-  uint32_t voff_pa, voff_pb;   // prefetch: row (64 w + lane) of A / of B
+  uint32_t voff_pa, voff_pb;   // prefetch: this lane's row of the tile's A / B prefetch share
   uint32_t lda, ldb, sstep_a, sstep_b;
   uint32_t k_begin;
   int wu;
@@ -242,16 +244,19 @@ __device__ __forceinline__ void issue_step(const TileDma& d, int ks, uint8_t* st
 }
 
 // L2 prefetch of K step ks: one 4-byte load per lane per operand touches
-// the 128-byte line that holds row (64 w + lane)'s K chunk of the step, so
-// that the step's DMA, issued two steps later, finds its lines in L2. The
-// loads go to a scratch LDS area that is never read: they need no register
-// and are not removed as dead.
+// the 128-byte line that holds a row's K chunk of the step, so that the
+// step's DMA, issued two steps later, finds its lines in L2. Workgroups that
+// run at the same time on one XCD share A and B tiles (see band_order); each
+// prefetches only its share of the rows, so a line is fetched about once per
+// XCD and the texture path (about 2 clocks per line touched) stays free for
+// the DMA. The loads go to a scratch LDS area that is never read: they need
+// no register and are not removed as dead.
 __device__ __forceinline__ void prefetch_step(const TileDma& d, int ks, uint8_t* sink) {
   const uint32_t kb = d.k_begin + (uint32_t)ks * kBK;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (__attribute__((address_space(3))) void*)sink, 4, d.voff_pa,
-                                           64 * d.wu * d.lda + kb, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rb, (__attribute__((address_space(3))) void*)sink, 4, d.voff_pb,
-                                           64 * d.wu * d.ldb + kb, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (__attribute__((address_space(3))) void*)sink, 4, d.voff_pa, kb, 0,
+                                           0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rb, (__attribute__((address_space(3))) void*)sink, 4, d.voff_pb, kb, 0,
+                                           0);
 }
 
 // Scale dwords of the lane's A and B row blocks in stage buffer `st`: byte
@@ -358,8 +363,10 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& ts) {
     d.voff_a[par] = (lane >> 3) * d.lda + 16 * piece;
     d.voff_b[par] = (lane >> 3) * d.ldb + 16 * piece;
   }
-  d.voff_pa = lane * d.lda;
-  d.voff_pb = lane * d.ldb;
+  // the 256 lanes of the workgroup spread over the share's rows
+  const uint32_t t = threadIdx.x;
+  d.voff_pa = (uint32_t)(ts.pf_a0 + ((t * (uint32_t)ts.pf_an) >> 8)) * d.lda;
+  d.voff_pb = (uint32_t)(ts.pf_b0 + ((t * (uint32_t)ts.pf_bn) >> 8)) * d.ldb;
 
   v16f acc[4][4];
 #pragma unroll
@@ -403,14 +410,29 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
 }
 
 // Tile index -> (row tile, column tile) in bands of kBandM row tiles, column
-// tiles walked within a band.
-__device__ __forceinline__ void band_order(int t, int mt, int nt, int& m, int& n) {
+// tiles walked within a band. `first` and `rows` return the band.
+__device__ __forceinline__ void band_order(int t, int mt, int nt, int& m, int& n, int& first, int& rows) {
   const int band = t / (kBandM * nt);
-  const int first = band * kBandM;
-  const int rows = min(kBandM, mt - first);
+  first = band * kBandM;
+  rows = min(kBandM, mt - first);
   const int r = t - band * kBandM * nt;
   m = first + r % rows;
   n = r / rows;
+}
+
+// Prefetch shares. Workgroups running together on an XCD hold consecutive
+// tile indices: up to kBandM row tiles of one band times about 4 column
+// tiles. An A row tile is thus shared by ~4 column tiles: column tile n takes
+// rows 64 (n % 4) .. + 63. A B column tile is shared by the `cnt` row tiles
+// of the band that use the same B (all of the band, or in a grouped GEMM the
+// band's tiles of one group); the row tile at position `idx` among them takes
+// the idx-th of cnt equal slices of its rows.
+__device__ __forceinline__ void set_prefetch_shares(TileSpec& ts, int n, int idx, int cnt) {
+  ts.pf_a0 = 64 * (n & 3);
+  ts.pf_an = 64;
+  const int part = (kBM + cnt - 1) / cnt;
+  ts.pf_b0 = idx * part;
+  ts.pf_bn = part;
 }
 
 // ---------------------------------------------------------------- groups
@@ -459,8 +481,8 @@ __device__ __forceinline__ int64_t group_start(const int32_t* ends, int g) {
 
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dense(GemmArgs a) {
   const int mt = (int)((a.M + kBM - 1) / kBM), nt = (int)((a.N + kBN - 1) / kBN);
-  int tm, tn;
-  band_order(xcd_remap(blockIdx.x, mt * nt), mt, nt, tm, tn);
+  int tm, tn, bfirst, brows;
+  band_order(xcd_remap(blockIdx.x, mt * nt), mt, nt, tm, tn, bfirst, brows);
   const int64_t m0 = (int64_t)tm * kBM;
   const int64_t n0 = (int64_t)tn * kBN;
   TileSpec ts;
@@ -479,6 +501,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dense(GemmArgs a) {
   ts.valid_n = (int)min<int64_t>(kBN, a.N - n0);
   ts.k_begin = 0;
   ts.nk = (int)steps;
+  set_prefetch_shares(ts, tn, tm - bfirst, brows);
   const int esz = a.out_f32 ? 4 : 2;
   ts.out = reinterpret_cast<uint8_t*>(a.out) + (m0 * a.ldo + n0) * esz;
   ts.ldo = a.ldo;
@@ -519,8 +542,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   const int mt = tile_end[a.E];
   const int nt = (int)((a.N + kBN - 1) / kBN);
   if ((int)blockIdx.x >= mt * nt) return;
-  int tile, tn;
-  band_order(xcd_remap(blockIdx.x, mt * nt), mt, nt, tile, tn);
+  int tile, tn, bfirst, brows;
+  band_order(xcd_remap(blockIdx.x, mt * nt), mt, nt, tile, tn, bfirst, brows);
   // first group whose row-tile range ends past `tile`
   int lo = 0, hi = a.E;
   while (lo < hi) {
@@ -549,6 +572,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   ts.valid_n = (int)min<int64_t>(kBN, a.N - n0);
   ts.k_begin = 0;
   ts.nk = g < a.E ? (int)(a.K / kBK) : 0;
+  {
+    // the band's row tiles that belong to group g share its B tiles
+    const int lo = max(bfirst, first), hi = min(bfirst + brows, tile_end[g]);
+    set_prefetch_shares(ts, tn, tile - lo, hi - lo);
+  }
   const int esz = a.out_f32 ? 4 : 2;
   ts.out = reinterpret_cast<uint8_t*>(a.out) + (m0 * a.ldo + n0) * esz;
   ts.ldo = a.ldo;
@@ -581,8 +609,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_wgrad(GemmArgs a) {
   }
   __syncthreads();
   const int g = pick;
-  int tn, tk;
-  band_order(u, nt_n, nt_k, tn, tk);
+  int tn, tk, bfirst, brows;
+  band_order(u, nt_n, nt_k, tn, tk, bfirst, brows);
   const int64_t ts0 = group_start(ends, g);
   const int64_t n0 = (int64_t)tn * kBM;   // rows of dW = rows of A (= N)
   const int64_t k0 = (int64_t)tk * kBN;   // cols of dW = rows of B (= K)
@@ -602,6 +630,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_wgrad(GemmArgs a) {
   ts.valid_n = (int)min<int64_t>(kBN, a.K - k0);
   ts.k_begin = ts0;
   ts.nk = (int)((ends[g] - ts0) / kBK);
+  set_prefetch_shares(ts, tk, tn - bfirst, brows);
   const int esz = a.out_f32 ? 4 : 2;
   ts.out = reinterpret_cast<uint8_t*>(a.out) + (g * a.out_group_stride + n0 * a.ldo + k0) * esz;
   ts.ldo = a.ldo;
