@@ -186,14 +186,16 @@ __device__ __forceinline__ void load_ops(const uint8_t* st, v8i (&av)[4], v8i (&
 }
 
 // 4 x 4 MFMAs of sub-step S; its scales are byte 2 S of the scale dwords
-// shifted right by 8 h (see the layout note at the top).
+// shifted right by hs = 8 h (see the layout note at the top). The dwords are
+// kept as read and shifted here, so no wait for the scale reads lands in the
+// middle of the phase that issues them.
 template <int S>
 __device__ __forceinline__ void mfmas(const v8i (&av)[4], const v8i (&bv)[4], const uint32_t (&sva)[4],
-                                      const uint32_t (&svb)[4], v16f (&acc)[4][4]) {
+                                      const uint32_t (&svb)[4], uint32_t hs, v16f (&acc)[4][4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mfma_mx<2 * S>(av[i], bv[j], acc[i][j], sva[i], svb[j]);
+    for (int j = 0; j < 4; ++j) acc[i][j] = mfma_mx<2 * S>(av[i], bv[j], acc[i][j], sva[i] >> hs, svb[j] >> hs);
 }
 
 // Barrier between the waves of the workgroup that neither waits for nor
@@ -260,16 +262,16 @@ __device__ __forceinline__ void prefetch_step(const TileDma& d, int ks, uint8_t*
 }
 
 // Scale dwords of the lane's A and B row blocks in stage buffer `st`: byte
-// 2 S + h of each serves sub-step S (after the shift by 8 h).
+// 2 S + h of each serves sub-step S (mfmas shifts by 8 h).
 __device__ __forceinline__ void load_scales(const uint8_t* st, uint32_t (&sva)[4], uint32_t (&svb)[4], int wm,
                                             int wn, int lane) {
   const uint32_t* SA = reinterpret_cast<const uint32_t*>(st + kStageA + kStageB);
   const uint32_t* SB = SA + kBM;
-  const int lrow = lane & 31, h = lane >> 5;
+  const int lrow = lane & 31;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    sva[i] = SA[wm * 128 + 32 * i + lrow] >> (8 * h);
-    svb[i] = SB[wn * 128 + 32 * i + lrow] >> (8 * h);
+    sva[i] = SA[wm * 128 + 32 * i + lrow];
+    svb[i] = SB[wn * 128 + 32 * i + lrow];
   }
 }
 
@@ -309,7 +311,7 @@ __device__ __forceinline__ void interleave() {
 __device__ __forceinline__ void step_full(const TileDma& d, int ks, int nk, uint8_t* cur, uint8_t* nxt, Regs& r,
                                           v16f (&acc)[4][4], int wm, int wn, int lane, uint8_t* sink) {
   __builtin_amdgcn_sched_barrier(0);
-  mfmas<0>(r.a0, r.b0, r.sva, r.svb, acc);
+  mfmas<0>(r.a0, r.b0, r.sva, r.svb, 8 * (lane >> 5), acc);
   load_ops<1>(cur, r.a1, r.b1, wm, wn, lane);
   interleave<1, 0>();
   __builtin_amdgcn_sched_barrier(0);
@@ -318,7 +320,7 @@ __device__ __forceinline__ void step_full(const TileDma& d, int ks, int nk, uint
   __builtin_amdgcn_sched_barrier(0);
   issue_step(d, ks + 2 < nk ? ks + 2 : nk - 1, cur);
   if constexpr (kPrefetch) prefetch_step(d, ks + 4 < nk ? ks + 4 : nk - 1, sink);
-  mfmas<1>(r.a1, r.b1, r.sva, r.svb, acc);
+  mfmas<1>(r.a1, r.b1, r.sva, r.svb, 8 * (lane >> 5), acc);
   load_ops<0>(nxt, r.a0, r.b0, wm, wn, lane);
   load_scales(nxt, r.nsa, r.nsb, wm, wn, lane);
   interleave<2, 2>();
