@@ -4,8 +4,10 @@
 //   E4M3 ("E4M3FN") code: sign | 4-bit exponent (bias 7) | 3-bit mantissa,
 //     subnormals m/8 * 2^-6, largest finite 448 = 0x7E, 0x7F/0xFF NaN.
 //   E8M0 scale byte b: 2^(b - 127), 0xFF NaN.
-// Everything here is exact integer/bit arithmetic except the E4M3 rounding,
-// which is round-to-nearest-even done on float32 bit patterns.
+// Everything here is exact integer/bit arithmetic except the E4M3 rounding:
+// round-to-nearest-even, done by gfx950's scaled conversion instruction on
+// the quantization path (e4m3_chunk, cvt4) and on float32 bit patterns in
+// e4m3_code.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -89,19 +91,60 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
   return (a < 0.015625f ? sub : nrm) | ((u >> 24) & 0x80u);
 }
 
-// Codes of the 8 bf16 values of a chunk, scaled by `mul` = 2^-E, packed
-// little-endian into 8 bytes. A block with scale 0xFF encodes 0x7F | sign.
-__device__ __forceinline__ uint2 e4m3_chunk(uint4 v, float mul, bool nonfinite) {
+// ---------------------------------------------------------------- E4M3 (hardware)
+//
+// gfx950's v_cvt_scalef32_pk_fp8_bf16 converts two bf16 values x to E4M3
+// codes of x / scale, rounded to nearest even, with the sign kept; measured
+// on the device, it equals the rounding above for every finite bf16 input
+// and every scale 2^E, E in [-127, 127] (including subnormal inputs and the
+// subnormal scale 2^-127) whenever |x / scale| <= 448. Above 448 it returns
+// NaN, so saturation clamps the magnitudes first (only FLOOR scales can put
+// elements above 448). Non-finite inputs give 0x7F | sign.
+
+typedef short mx_v2s __attribute__((ext_vector_type(2)));
+typedef __bf16 mx_v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned short mx_us2 __attribute__((ext_vector_type(2)));
+
+// 2^E as a float32 for a finite scale byte b = E + 127 (2^-127 is subnormal).
+__device__ __forceinline__ float scale_f32(uint32_t b) {
+  return __uint_as_float(b ? (b << 23) : 0x00400000u);
+}
+
+// bf16 bits of 448 * 2^E (infinity when that overflows bf16, which then
+// clamps nothing).
+__device__ __forceinline__ uint32_t sat_bits(uint32_t b) {
+  return b + 8u >= 255u ? 0x7F80u : (((b + 8u) << 7) | 0x60u);
+}
+
+// Clamps the magnitudes of the two bf16 values in w to lim2 (one 16-bit
+// limit per half), keeping the signs.
+__device__ __forceinline__ uint32_t clamp_pair(uint32_t w, uint32_t lim2) {
+  const mx_us2 m = __builtin_elementwise_min(__builtin_bit_cast(mx_us2, w & 0x7FFF7FFFu),
+                                             __builtin_bit_cast(mx_us2, lim2));
+  return (w & 0x80008000u) | __builtin_bit_cast(uint32_t, m);
+}
+
+// Codes of 4 bf16 values (pairs w0 = elements 0, 1 and w1 = 2, 3) divided by
+// `scale`, little-endian in one dword.
+__device__ __forceinline__ uint32_t cvt4(uint32_t w0, uint32_t w1, float scale) {
+  mx_v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(mx_v2s{0, 0}, __builtin_bit_cast(mx_v2bf, w0), scale, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(mx_v2bf, w1), scale, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Codes of the 8 bf16 values of a chunk under scale byte sb, packed
+// little-endian into 8 bytes; `saturate` clamps to 448 * 2^E first (needed
+// for FLOOR). A block with scale 0xFF encodes 0x7F | sign.
+__device__ __forceinline__ uint2 e4m3_chunk(uint4 v, uint32_t sb, bool saturate) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t out[2];
+  const bool nonfinite = sb == 0xFFu;
+  const float scale = scale_f32(sb);
+  if (saturate) {
+    const uint32_t lim = sat_bits(sb);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    uint32_t c0 = e4m3_code(bf16_lo(w[2 * i]) * mul);
-    uint32_t c1 = e4m3_code(bf16_hi(w[2 * i]) * mul);
-    uint32_t c2 = e4m3_code(bf16_lo(w[2 * i + 1]) * mul);
-    uint32_t c3 = e4m3_code(bf16_hi(w[2 * i + 1]) * mul);
-    out[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    for (int i = 0; i < 4; ++i) w[i] = clamp_pair(w[i], lim | (lim << 16));
   }
+  uint32_t out[2] = {cvt4(w[0], w[1], scale), cvt4(w[2], w[3], scale)};
   if (nonfinite) {
     // 0x7F with each element's sign (bit 15 of each bf16)
     uint32_t s0 = ((w[0] >> 8) & 0x80u) | ((w[0] >> 16) & 0x8000u) | ((w[1] << 8) & 0x800000u) | (w[1] & 0x80000000u);

@@ -53,7 +53,7 @@ __device__ __forceinline__ void tile_rowq(const uint4 (&v)[kTileChunks], int row
   for (int j = 0; j < kTileChunks; ++j) {
     const int row = (t >> 4) + 16 * j;
     const uint32_t sb = scale_byte(quad_max(absmax8_bits(v[j])), rceil);
-    const uint2 codes = e4m3_chunk(v[j], inv_scale(sb), sb == 0xFFu);
+    const uint2 codes = e4m3_chunk(v[j], sb, !rceil);
     uint32_t packed = 0;
     if (o.k128) {
       packed = sb << (8 * (cc >> 2));
@@ -102,17 +102,20 @@ __device__ __forceinline__ void tile_colq(const uint4* lds4, int rows_valid, int
     m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w[i] & 0x7FFF7FFFu));
   const uint32_t sb0 = scale_byte(m.x, rceil);
   const uint32_t sb1 = scale_byte(m.y, rceil);
-  const float mul0 = inv_scale(sb0), mul1 = inv_scale(sb1);
+  const float sc0 = scale_f32(sb0), sc1 = scale_f32(sb1);
+  if (!rceil) {
+    const uint32_t lim2 = sat_bits(sb0) | (sat_bits(sb1) << 16);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) w[i] = clamp_pair(w[i], lim2);
+  }
   uint32_t c0w[8], c1w[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    uint32_t a0 = 0, a1 = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t x = w[4 * k + i];
-      a0 |= e4m3_code(bf16_lo(x) * mul0) << (8 * i);
-      a1 |= e4m3_code(bf16_hi(x) * mul1) << (8 * i);
-    }
+    // pairs of consecutive rows of one column: low halves (column 2p), high
+    // halves (column 2p + 1)
+    const uint32_t* x = &w[4 * k];
+    uint32_t a0 = cvt4(__builtin_amdgcn_perm(x[1], x[0], 0x05040100u), __builtin_amdgcn_perm(x[3], x[2], 0x05040100u), sc0);
+    uint32_t a1 = cvt4(__builtin_amdgcn_perm(x[1], x[0], 0x07060302u), __builtin_amdgcn_perm(x[3], x[2], 0x07060302u), sc1);
     if (sb0 == 0xFFu) {
       a0 = 0x7F7F7F7Fu;
 #pragma unroll
