@@ -10,10 +10,10 @@
 // 8 (t & 15) .. 8 (t & 15) + 7, so the 4 lanes of a quad hold one 32-value
 // row block and the block maximum is two DPP quad permutes away.
 // Row-wise quantization is done straight from registers. For column-wise
-// quantization the tile is written to LDS (dword = two adjacent columns) and
-// each thread reads one 32-row block of a column pair back: 64 lanes read 64
-// consecutive dwords per row, which is free of bank conflicts, and each lane
-// then writes 32 contiguous code bytes per column.
+// quantization the tile is written to LDS (XOR-swizzled 16-byte units) and
+// each lane reads back 16 rows of a column pair (one dword per row); the 8
+// lanes of a column pair together hold one 128-code output row, so every
+// store instruction writes whole 128-byte lines.
 //
 // The fused SwiGLU kernels produce their tile in registers from the inputs
 // (h = silu(a) * b, or dA / dB), round it to bf16 and run the same two
@@ -73,77 +73,96 @@ __device__ __forceinline__ void tile_rowq(const uint4 (&v)[kTileChunks], int row
   }
 }
 
-// Stage the thread's chunks in LDS (row-major, 64 dwords per tile row).
+// Stage the thread's chunks in LDS: tile row r, 16-byte unit u (columns
+// 8 u .. 8 u + 7) at slot r * 16 + (u ^ g(r)), g(r) = 2 ((r >> 4) & 7). A
+// ds_write_b128 pass (16 lanes = one row) covers the 64 banks once.
+__device__ __forceinline__ int lds_unit(int r, int u) { return r * 16 + (u ^ (((r >> 4) & 7) << 1)); }
+
 __device__ __forceinline__ void tile_to_lds(const uint4 (&v)[kTileChunks], uint4* lds) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < kTileChunks; ++j) lds[((t >> 4) + 16 * j) * (kTC / 8) + (t & 15)] = v[j];
+  for (int j = 0; j < kTileChunks; ++j) lds[lds_unit((t >> 4) + 16 * j, t & 15)] = v[j];
 }
 
-// Column-wise quantization from the LDS tile: thread t takes columns
-// 2p, 2p+1 (p = t & 63) and rows 32 b .. 32 b + 31 (b = t >> 6) of the tile,
-// i.e. one output block in each of two output rows. Output row = tile
-// column c0 + col, output column = tile row r0 + row. In the k128 layout
-// (r0 % 128 == 0) block b is byte b of the output row's step dword.
+// Column-wise quantization from the LDS tile. Work item (cp, q): columns
+// 2 cp, 2 cp + 1 and tile rows 16 q .. 16 q + 15, i.e. half a 32-row block of
+// two output rows. Lane l of wave w takes q = l & 7 and, in pass s, column
+// pair cp = 8 (4 s + w) + (l >> 3): the 8 lanes of a column pair cover one
+// output row's 128 codes, so each 16-byte store writes 8 whole lines. Block
+// maxima pair lanes q, q ^ 1 (one DPP exchange). The LDS reads (one dword =
+// two columns, 16 rows) hit 64 distinct banks thanks to the swizzle above.
+// Output row = tile column c0 + col, output column = tile row r0 + row.
+// All lanes must reach this function.
 __device__ __forceinline__ void tile_colq(const uint4* lds4, int rows_valid, int cols_valid,
                                           bool rceil, TileOut o, int64_t r0, int64_t c0) {
   const uint32_t* lds = reinterpret_cast<const uint32_t*>(lds4);
-  const int t = threadIdx.x;
-  const int p = t & 63;
-  const int b = t >> 6;
-  if (2 * p >= cols_valid || 32 * b >= rows_valid) return;
-  uint32_t w[32];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane & 7;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) w[i] = lds[(32 * b + i) * (kTC / 2) + p];
-  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-  us2 m = __builtin_bit_cast(us2, w[0] & 0x7FFF7FFFu);
+  for (int s = 0; s < 2; ++s) {
+    const int cp = 8 * (4 * s + w) + (lane >> 3);
+    uint32_t v[16];
 #pragma unroll
-  for (int i = 1; i < 32; ++i)
-    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w[i] & 0x7FFF7FFFu));
-  const uint32_t sb0 = scale_byte(m.x, rceil);
-  const uint32_t sb1 = scale_byte(m.y, rceil);
-  const float sc0 = scale_f32(sb0), sc1 = scale_f32(sb1);
-  if (!rceil) {
-    const uint32_t lim2 = sat_bits(sb0) | (sat_bits(sb1) << 16);
+    for (int r = 0; r < 16; ++r) v[r] = lds[lds_unit(16 * q + r, cp >> 2) * 4 + (cp & 3)];
+    mx_us2 m = __builtin_bit_cast(mx_us2, v[0] & 0x7FFF7FFFu);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) w[i] = clamp_pair(w[i], lim2);
-  }
-  uint32_t c0w[8], c1w[8];
+    for (int r = 1; r < 16; ++r) m = __builtin_elementwise_max(m, __builtin_bit_cast(mx_us2, v[r] & 0x7FFF7FFFu));
+    uint32_t mm = __builtin_bit_cast(uint32_t, m);
+    const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)mm, 0xB1, 0xF, 0xF, false);   // lane ^ 1
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(mx_us2, other));
+    const uint32_t sb0 = scale_byte(m.x, rceil);
+    const uint32_t sb1 = scale_byte(m.y, rceil);
+    if (!rceil) {
+      const uint32_t lim2 = sat_bits(sb0) | (sat_bits(sb1) << 16);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    // pairs of consecutive rows of one column: low halves (column 2p), high
-    // halves (column 2p + 1)
-    const uint32_t* x = &w[4 * k];
-    uint32_t a0 = cvt4(__builtin_amdgcn_perm(x[1], x[0], 0x05040100u), __builtin_amdgcn_perm(x[3], x[2], 0x05040100u), sc0);
-    uint32_t a1 = cvt4(__builtin_amdgcn_perm(x[1], x[0], 0x07060302u), __builtin_amdgcn_perm(x[3], x[2], 0x07060302u), sc1);
-    if (sb0 == 0xFFu) {
-      a0 = 0x7F7F7F7Fu;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a0 |= ((w[4 * k + i] >> 15) & 1u) << (8 * i + 7);
+      for (int r = 0; r < 16; ++r) v[r] = clamp_pair(v[r], lim2);
     }
-    if (sb1 == 0xFFu) {
-      a1 = 0x7F7F7F7Fu;
+    const float sc0 = scale_f32(sb0), sc1 = scale_f32(sb1);
+    uint32_t c0w[4], c1w[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a1 |= ((w[4 * k + i] >> 31) & 1u) << (8 * i + 7);
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t* x = &v[4 * k];
+      c0w[k] = cvt4(__builtin_amdgcn_perm(x[1], x[0], 0x05040100u), __builtin_amdgcn_perm(x[3], x[2], 0x05040100u), sc0);
+      c1w[k] = cvt4(__builtin_amdgcn_perm(x[1], x[0], 0x07060302u), __builtin_amdgcn_perm(x[3], x[2], 0x07060302u), sc1);
+      if (sb0 == 0xFFu) {
+        uint32_t a = 0x7F7F7F7Fu;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a |= ((x[i] >> 15) & 1u) << (8 * i + 7);
+        c0w[k] = a;
+      }
+      if (sb1 == 0xFFu) {
+        uint32_t a = 0x7F7F7F7Fu;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a |= ((x[i] >> 31) & 1u) << (8 * i + 7);
+        c1w[k] = a;
+      }
     }
-    c0w[k] = a0;
-    c1w[k] = a1;
-  }
-  const int64_t orow0 = c0 + 2 * p;
-  const int64_t ocol = r0 + 32 * b;
-  uint4* d0 = reinterpret_cast<uint4*>(o.q + orow0 * o.ld + ocol);
-  uint4* d1 = reinterpret_cast<uint4*>(o.q + (orow0 + 1) * o.ld + ocol);
-  d0[0] = make_uint4(c0w[0], c0w[1], c0w[2], c0w[3]);
-  d0[1] = make_uint4(c0w[4], c0w[5], c0w[6], c0w[7]);
-  d1[0] = make_uint4(c1w[0], c1w[1], c1w[2], c1w[3]);
-  d1[1] = make_uint4(c1w[4], c1w[5], c1w[6], c1w[7]);
-  if (o.k128) {
-    uint8_t* sd = o.s + ((r0 >> 7) * o.srows + orow0) * 4 + b;
-    sd[0] = (uint8_t)sb0;
-    sd[4] = (uint8_t)sb1;
-  } else {
-    o.s[orow0 * (o.ld / kBlock) + ocol / kBlock] = (uint8_t)sb0;
-    o.s[(orow0 + 1) * (o.ld / kBlock) + ocol / kBlock] = (uint8_t)sb1;
+    // scale bytes of the step's four blocks for the two output rows
+    uint32_t p0 = 0, p1 = 0;
+    if (o.k128) {
+      p0 = sb0 << (8 * (q >> 1));
+      p1 = sb1 << (8 * (q >> 1));
+      p0 |= (uint32_t)__shfl_xor((int)p0, 2);
+      p1 |= (uint32_t)__shfl_xor((int)p1, 2);
+      p0 |= (uint32_t)__shfl_xor((int)p0, 4);
+      p1 |= (uint32_t)__shfl_xor((int)p1, 4);
+    }
+    if (2 * cp < cols_valid && 16 * q < rows_valid) {
+      const int64_t orow0 = c0 + 2 * cp;
+      const int64_t ocol = r0 + 16 * q;
+      *reinterpret_cast<uint4*>(o.q + orow0 * o.ld + ocol) = make_uint4(c0w[0], c0w[1], c0w[2], c0w[3]);
+      *reinterpret_cast<uint4*>(o.q + (orow0 + 1) * o.ld + ocol) = make_uint4(c1w[0], c1w[1], c1w[2], c1w[3]);
+      if (o.k128) {
+        if (q == 0) {
+          uint32_t* sd = reinterpret_cast<uint32_t*>(o.s + ((r0 >> 7) * o.srows + orow0) * 4);
+          sd[0] = p0;
+          sd[1] = p1;
+        }
+      } else if ((q & 1) == 0) {
+        o.s[orow0 * (o.ld / kBlock) + ocol / kBlock] = (uint8_t)sb0;
+        o.s[(orow0 + 1) * (o.ld / kBlock) + ocol / kBlock] = (uint8_t)sb1;
+      }
+    }
   }
 }
 
