@@ -195,8 +195,10 @@ __device__ __forceinline__ void tile_store_bf16(const uint4 (&v)[kTileChunks], u
 
 // ---------------------------------------------------------------- quantize
 
+// COL: column-wise output requested (the LDS tile exists only then, so the
+// row-only kernel keeps more workgroups resident).
+template <bool COL>
 __global__ __launch_bounds__(kTileThreads) void k_quant_tile(QuantArgs a) {
-  __shared__ uint4 lds[kTR * kTC / 8];
   const int64_t bz = blockIdx.z;
   const int64_t r0 = (int64_t)blockIdx.y * kTR;
   const int64_t c0 = (int64_t)blockIdx.x * kTC;
@@ -208,7 +210,8 @@ __global__ __launch_bounds__(kTileThreads) void k_quant_tile(QuantArgs a) {
     TileOut o{a.q_row + bz * a.rows * a.cols, a.s_row + bz * a.rows * (a.cols / kBlock), a.cols, a.rows, a.k128};
     tile_rowq(v, rows_valid, cols_valid, a.rceil, o, r0, c0);
   }
-  if (a.q_col) {
+  if constexpr (COL) {
+    __shared__ uint4 lds[kTR * kTC / 8];
     tile_to_lds(v, lds);
     __syncthreads();
     TileOut o{a.q_col + bz * a.rows * a.cols, a.s_col + bz * a.cols * (a.rows / kBlock), a.rows, a.cols, a.k128};
@@ -354,7 +357,10 @@ namespace mxk {
 hipError_t launch_quant(const QuantArgs& a, int64_t batch, hipStream_t s) {
   dim3 grid((unsigned)((a.cols + kTC - 1) / kTC), (unsigned)((a.rows + kTR - 1) / kTR),
             (unsigned)batch);
-  hipLaunchKernelGGL(k_quant_tile, grid, dim3(kTileThreads), 0, s, a);
+  if (a.q_col)
+    hipLaunchKernelGGL(k_quant_tile<true>, grid, dim3(kTileThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_quant_tile<false>, grid, dim3(kTileThreads), 0, s, a);
   return hipGetLastError();
 }
 
