@@ -289,13 +289,20 @@ mx_status mx_grouped_mm_wgrad_hp(const void* g, const void* x, const int32_t* of
   MX_REQUIRE(E >= 1 && E <= 1024, MX_ERR_SHAPE, "%s: E must be in [1, 1024]", fn);
   MX_REQUIRE(Tcap >= 0 && Tcap % 128 == 0, MX_ERR_SHAPE, "%s: Tcap must be a multiple of 128", fn);
   MX_REQUIRE(N > 0 && N % 16 == 0 && K > 0 && K % 16 == 0, MX_ERR_SHAPE, "%s: N and K must be positive multiples of 16", fn);
-  MX_REQUIRE((N + 127) / 128 <= 65535 && (K + 127) / 128 <= 65535, MX_ERR_SHAPE, "%s: too large", fn);
+  MX_REQUIRE((N + 255) / 256 * ((K + 255) / 256) * E <= 0x7FFFFFFF, MX_ERR_SHAPE, "%s: too large", fn);
+  // the kernel addresses each operand with 32-bit buffer offsets
+  MX_REQUIRE(Tcap * N * 2 < (1ll << 31) && Tcap * K * 2 < (1ll << 31), MX_ERR_SHAPE, "%s: operands too large", fn);
   MX_REQUIRE(g && x && offs && out, MX_ERR_NULL, "%s: NULL pointer", fn);
   MX_REQUIRE(al16(g) && al16(x) && al16(out), MX_ERR_ALIGN, "%s: g/x/out must be 16-byte aligned", fn);
   MX_DEVICE();
-  mxk::HpWgradArgs a{static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(x), offs, E, Tcap, N, K,
-                     static_cast<uint16_t*>(out), dev_err};
-  return launched(mxk::launch_hp_wgrad(a, as_stream(stream)), fn);
+  mxk::GemmArgs a{};
+  a.qa = static_cast<const uint8_t*>(g); a.qb = static_cast<const uint8_t*>(x);
+  a.M = Tcap; a.N = N; a.K = K;
+  a.lda = 2 * N; a.ldb = 2 * K;
+  a.out_group_stride = N * K;
+  a.out = out; a.ldo = K; a.out_f32 = false;
+  a.offs = offs; a.E = E; a.dev_err = dev_err;
+  return launched(mxk::launch_gemm_wgrad_hp(a, as_stream(stream)), fn);
 }
 
 mx_status mx_pad_groups(const void* x, const int32_t* group_sizes, int32_t E, int64_t T, int64_t row_bytes,

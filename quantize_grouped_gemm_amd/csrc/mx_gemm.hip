@@ -9,7 +9,9 @@
 //   k_gemm_grouped  2-D x 3-D: row tiles of A belong to one expert group and
 //                   multiply that expert's B (grouped fwd and dgrad)
 //   k_gemm_wgrad    2-D x 2-D: per expert, the contraction runs over the
-//                   group's own token range (grouped weight gradient)
+//                   group's own token range (grouped weight gradient); its
+//                   bf16 instance is the wgrad_with_hp GEMM (see "bf16
+//                   wgrad" below)
 //
 // Tile routine: a 256-thread workgroup computes a 256 x 256 output tile in
 // K steps of 128 (four scale blocks, two MFMA K sub-steps). Waves form a
@@ -403,6 +405,179 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& ts) {
   store_tile(acc, ts, mine);
 }
 
+// ---------------------------------------------------------------- bf16 wgrad
+//
+// The wgrad_with_hp GEMM dW[g] = G[s:e]^T X[s:e] on the unquantized bf16
+// operands, whose contraction axis (tokens) is the strided one: G [Tcap, N]
+// and X [Tcap, K] row-major. Same 256 x 256 tiles, waves, tile order and
+// two-stage DMA as above, with v_mfma_f32_32x32x16_bf16 and K steps of 64
+// tokens. A stage holds each operand as loaded: 64 token rows x 256 columns
+// x 2 bytes (32 units of 16 bytes per row). The MFMA wants each lane to hold
+// 8 consecutive tokens of one column. gfx950's transposing LDS read
+// (ds_read_b64_tr_b16) delivers them: within each group of 16 lanes, lane j
+// receives element j % 4 of the 8-byte chunks that lanes 4 e + j / 4
+// (e = 0..3) address (measured on the device). Lane 4 e + q of a group thus
+// addresses columns 4 q .. 4 q + 3 of the group's 16 in token row e, and
+// lane j gets 4 tokens of column j; two reads give the 8. Unit u of token
+// row t sits at slot u ^ (4 (t % 4)), so the 4 token rows and 4 units that a
+// 32-lane pass touches cover the 64 banks once.
+constexpr int kHpT = 64;                  // tokens per K step
+constexpr int kHpRowB = 512;              // LDS bytes per token row (256 columns)
+constexpr int kHpPart = kHpT * kHpRowB;   // 32 KB per operand and stage
+static_assert(2 * kHpPart <= kStageBytes, "an hp stage fits a stage buffer");
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+struct HpDma {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t voff_a[2], voff_b[2];   // lane offsets for even / odd instructions
+  uint32_t lda, ldb;               // bytes per token row of G / of X
+  uint32_t t_begin;
+  int wu;
+};
+
+// One 16-byte-per-lane LDS DMA (64 lanes x 16 bytes to lds_dst onwards),
+// written as inline assembly: the compiler does not track it, so it inserts
+// no wait for it before the transposing LDS reads (whose memory operands
+// carry no alias information and would otherwise wait for every DMA in
+// flight). The step loop orders DMA and reads itself: explicit s_waitcnt
+// vmcnt before each workgroup barrier. Nothing else in this kernel uses M0.
+__device__ __forceinline__ void dma16(const __amdgpu_buffer_rsrc_t& r, const uint8_t* lds_dst, uint32_t voff,
+                                      uint32_t soff) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(const_cast<uint8_t*>(lds_dst));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(r),
+               "s"(soff));
+}
+
+// DMA of K step ks (64 tokens) of both operands into stage `st` (G part,
+// then X part). Instruction i of wave w covers token rows 16 w + 2 i and
+// 16 w + 2 i + 1; lane l writes slot l & 31 of row + (l >> 5), i.e. global
+// unit (l & 31) ^ (4 ((2 i + (l >> 5)) % 4)).
+__device__ __forceinline__ void issue_hp(const HpDma& d, int ks, uint8_t* st) {
+  const uint32_t t0 = d.t_begin + (uint32_t)ks * kHpT;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t row = 16 * d.wu + 2 * i;
+    dma16(d.ra, st + row * kHpRowB, d.voff_a[i & 1], (t0 + row) * d.lda);
+    dma16(d.rb, st + kHpPart + row * kHpRowB, d.voff_b[i & 1], (t0 + row) * d.ldb);
+  }
+}
+
+__device__ __forceinline__ v4s tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(const_cast<uint8_t*>(p)));
+}
+
+// MFMA operands of 16-token sub-step S (0..3) of a part for the wave's 128
+// columns (half `whalf` of the 256): block i = columns 32 i .. 32 i + 31.
+template <int S>
+__device__ __forceinline__ void read_hp(const uint8_t* part, v8bf (&o)[4], int whalf, int lane) {
+  const int g = lane >> 4, j = lane & 15, e = j >> 2;
+  const int trow = 16 * S + 8 * (g >> 1) + e;   // t % 4 == e
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = 16 * whalf + 4 * i + 2 * (g & 1) + ((j & 3) >> 1);
+    const uint8_t* p = part + trow * kHpRowB + ((u ^ (4 * e)) << 4) + 8 * (j & 1);
+    const v4s lo = tr16(p), hi = tr16(p + 4 * kHpRowB);
+    o[i] = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
+template <int S>
+__device__ __forceinline__ void mfmas_hp(const v8bf (&a)[4], const v8bf (&b)[4], v16f (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+struct HpRegs {
+  v8bf a[4][4], b[4][4];   // [sub-step][block]
+};
+
+// One K step ks from stage `cur` (sub-steps 0, 1 already in registers);
+// `nxt` receives step ks+1's DMA after the barrier at the start of the step.
+// Phase A: sub-steps 0, 1 multiply while 2, 3 are read from `cur`; barrier;
+// phase B: sub-steps 2, 3 multiply while step ks+1's 0, 1 are read from
+// `nxt`. Mirrors step_full of the MXFP8 tile.
+__device__ __forceinline__ void step_hp(const HpDma& d, int ks, int nk, uint8_t* cur, uint8_t* nxt, HpRegs& r,
+                                        v16f (&acc)[4][4], int wm, int wn, int lane) {
+  __builtin_amdgcn_sched_barrier(0);
+  mfmas_hp<0>(r.a[0], r.b[0], acc);
+  mfmas_hp<1>(r.a[1], r.b[1], acc);
+  read_hp<2>(cur, r.a[2], wm, lane);
+  read_hp<2>(cur + kHpPart, r.b[2], wn, lane);
+  read_hp<3>(cur, r.a[3], wm, lane);
+  read_hp<3>(cur + kHpPart, r.b[3], wn, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  MX_WAIT_VM_LDS(0);   // step ks+1 has landed (this wave) and the reads are done
+  wg_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  issue_hp(d, ks + 2 < nk ? ks + 2 : nk - 1, cur);
+  mfmas_hp<2>(r.a[2], r.b[2], acc);
+  mfmas_hp<3>(r.a[3], r.b[3], acc);
+  read_hp<0>(nxt, r.a[0], wm, lane);
+  read_hp<0>(nxt + kHpPart, r.b[0], wn, lane);
+  read_hp<1>(nxt, r.a[1], wm, lane);
+  read_hp<1>(nxt + kHpPart, r.b[1], wn, lane);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// ts.a / ts.b: column n0 of G / k0 of X (token row 0); ts.lda / ts.ldb: bytes
+// per token row; ts.sbytes_a / sbytes_b: bytes from ts.a / ts.b to the end
+// of the operand; ts.k_begin: first token; ts.nk: 64-token steps (even).
+__device__ __forceinline__ void gemm_tile_hp(const TileSpec& ts) {
+  __shared__ __align__(16) uint8_t hs0[kStageBytes];
+  __shared__ __align__(16) uint8_t hs1[kStageBytes];
+  if (ts.nk <= 0) {
+    zero_tile(ts);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  HpDma d;
+  d.wu = __builtin_amdgcn_readfirstlane(w);
+  // columns past N (K) read other rows' values or 0 past the end: they only
+  // reach dW rows (columns) that are not stored
+  d.ra = __builtin_amdgcn_make_buffer_rsrc((void*)ts.a, (short)0, (int)ts.sbytes_a, 0x00020000);
+  d.rb = __builtin_amdgcn_make_buffer_rsrc((void*)ts.b, (short)0, (int)ts.sbytes_b, 0x00020000);
+  d.lda = (uint32_t)ts.lda;
+  d.ldb = (uint32_t)ts.ldb;
+  d.t_begin = (uint32_t)ts.k_begin;
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const uint32_t unit = (lane & 31) ^ (4 * ((2 * par + (lane >> 5)) & 3));
+    d.voff_a[par] = (lane >> 5) * d.lda + 16 * unit;
+    d.voff_b[par] = (lane >> 5) * d.ldb + 16 * unit;
+  }
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+  const int nk = ts.nk;
+  issue_hp(d, 0, hs0);
+  issue_hp(d, 1 < nk ? 1 : nk - 1, hs1);
+  MX_WAIT_VM_LDS(16);   // step 0 has landed
+  wg_barrier();
+  HpRegs r;
+  read_hp<0>(hs0, r.a[0], wm, lane);
+  read_hp<0>(hs0 + kHpPart, r.b[0], wn, lane);
+  read_hp<1>(hs0, r.a[1], wm, lane);
+  read_hp<1>(hs0 + kHpPart, r.b[1], wn, lane);
+  int ks = 0;
+  for (; ks + 1 < nk; ks += 2) {
+    step_hp(d, ks, nk, hs0, hs1, r, acc, wm, wn, lane);
+    step_hp(d, ks + 1, nk, hs1, hs0, r, acc, wm, wn, lane);
+  }
+  if (ks < nk) step_hp(d, ks, nk, hs0, hs1, r, acc, wm, wn, lane);
+  MX_WAIT_VM_LDS(0);
+  wg_barrier();
+  uint8_t* mine = (w & 1 ? hs1 : hs0) + (w >> 1) * (64 * 132 * 4);
+  store_tile(acc, ts, mine);
+}
+
 // Maps the linear index of a workgroup (dispatched round-robin over the 8
 // XCDs) to a tile index so that each XCD gets a contiguous run of tiles.
 __device__ __forceinline__ int xcd_remap(int b, int total) {
@@ -589,6 +764,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
 // The grid covers E x (N tiles) x (K tiles) of dW. Tile indices run over the
 // groups ranked by token count, largest first (the longest tiles start
 // first); within a group's [N, K] rectangle tiles follow the band order.
+// HP: the bf16 wgrad_with_hp operands (G, X as [Tcap, N], [Tcap, K]); else
+// the MXFP8 column-wise operands ([N, Tcap], [K, Tcap] codes).
+template <bool HP>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_wgrad(GemmArgs a) {
   __shared__ int32_t ends[kMaxGroups + 1];
   __shared__ int32_t pick;
@@ -618,26 +796,36 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_wgrad(GemmArgs a) {
   const int64_t k0 = (int64_t)tk * kBN;   // cols of dW = rows of B (= K)
   TileSpec ts;
   const int64_t steps = a.M / kBK;   // 128-token steps of Tcap
-  ts.a = a.qa + n0 * a.lda;
-  ts.sa = a.sa + n0 * 4;
-  ts.b = a.qb + k0 * a.ldb;
-  ts.sb = a.sb + k0 * 4;
+  if constexpr (HP) {
+    ts.a = a.qa + n0 * 2;
+    ts.b = a.qb + k0 * 2;
+    ts.sbytes_a = a.M * a.lda - n0 * 2;
+    ts.sbytes_b = a.M * a.ldb - k0 * 2;
+  } else {
+    ts.a = a.qa + n0 * a.lda;
+    ts.sa = a.sa + n0 * 4;
+    ts.b = a.qb + k0 * a.ldb;
+    ts.sb = a.sb + k0 * 4;
+    ts.sstep_a = 4 * a.srows_a;
+    ts.sstep_b = 4 * a.srows_b;
+    ts.sbytes_a = steps * ts.sstep_a - n0 * 4;
+    ts.sbytes_b = steps * ts.sstep_b - k0 * 4;
+  }
   ts.lda = a.lda;
   ts.ldb = a.ldb;
-  ts.sstep_a = 4 * a.srows_a;
-  ts.sstep_b = 4 * a.srows_b;
-  ts.sbytes_a = steps * ts.sstep_a - n0 * 4;
-  ts.sbytes_b = steps * ts.sstep_b - k0 * 4;
   ts.valid_m = (int)min<int64_t>(kBM, a.N - n0);
   ts.valid_n = (int)min<int64_t>(kBN, a.K - k0);
   ts.k_begin = ts0;
-  ts.nk = (int)((ends[g] - ts0) / kBK);
+  ts.nk = (int)((ends[g] - ts0) / (HP ? kHpT : kBK));
   set_prefetch_shares(ts, tk, tn - bfirst, brows);
   const int esz = a.out_f32 ? 4 : 2;
   ts.out = reinterpret_cast<uint8_t*>(a.out) + (g * a.out_group_stride + n0 * a.ldo + k0) * esz;
   ts.ldo = a.ldo;
   ts.out_f32 = a.out_f32;
-  gemm_tile(ts);
+  if constexpr (HP)
+    gemm_tile_hp(ts);
+  else
+    gemm_tile(ts);
 }
 
 // ---------------------------------------------------------------- launch
@@ -659,7 +847,13 @@ hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_wgrad(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles = ((a.K + kBN - 1) / kBN) * ((a.N + kBM - 1) / kBM) * a.E;
-  hipLaunchKernelGGL(k_gemm_wgrad, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a);
+  hipLaunchKernelGGL(k_gemm_wgrad<false>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_wgrad_hp(const GemmArgs& a, hipStream_t s) {
+  const int64_t tiles = ((a.K + kBN - 1) / kBN) * ((a.N + kBM - 1) / kBM) * a.E;
+  hipLaunchKernelGGL(k_gemm_wgrad<true>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -75,14 +75,6 @@ struct UnpadArgs {
   uint8_t* y;
 };
 
-struct HpWgradArgs {
-  const uint16_t *g, *x;
-  const int32_t* offs;
-  int32_t E;
-  int64_t Tcap, N, K;
-  uint16_t* out;
-  int32_t* dev_err;
-};
 
 // Launchers: return hipSuccess or the launch error. Shapes are validated by
 // the caller (mx_abi.cpp).
@@ -93,8 +85,10 @@ hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_wgrad(const GemmArgs& a, hipStream_t s);
+// bf16 wgrad_with_hp: qa / qb are G [M = Tcap, N] and X [Tcap, K] bf16,
+// lda / ldb their row pitches in bytes, out bf16 [E, N, K].
+hipError_t launch_gemm_wgrad_hp(const GemmArgs& a, hipStream_t s);
 hipError_t launch_pad(const PadArgs& a, hipStream_t s);
 hipError_t launch_unpad(const UnpadArgs& a, hipStream_t s);
-hipError_t launch_hp_wgrad(const HpWgradArgs& a, hipStream_t s);
 
 }  // namespace mxk

@@ -214,7 +214,7 @@ class MoEMLP:
                                                         self.hq["s_col"], self.offs, out=self.dw2,
                                                         dev_err=err)))
         else:
-            st.append(Stage("gemm_w2_wgrad_hp", "k_hp_wgrad", 2 * T * D * H, 0,
+            st.append(Stage("gemm_w2_wgrad_hp", "k_gemm_wgrad_hp", 2 * T * D * H, 0,
                             lambda: mx.grouped_mm_wgrad_hp(self.dy_pad, self.hq["h"], self.offs, out=self.dw2,
                                                            dev_err=err)))
         st += [
@@ -232,7 +232,7 @@ class MoEMLP:
                                                         self.qx["s_col"], self.offs, out=self.dw13,
                                                         dev_err=err)))
         else:
-            st.append(Stage("gemm_w13_wgrad_hp", "k_hp_wgrad", 2 * T * 2 * H * D, 0,
+            st.append(Stage("gemm_w13_wgrad_hp", "k_gemm_wgrad_hp", 2 * T * 2 * H * D, 0,
                             lambda: mx.grouped_mm_wgrad_hp(self.dzq["dab"], self.x_pad, self.offs,
                                                            out=self.dw13, dev_err=err)))
         return st
