@@ -94,58 +94,79 @@ __device__ __forceinline__ v8i cat8(uint4 x, uint4 y) {
   return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
 }
 
-// Epilogue: each wave stages its 128 x 128 float sub-tile through its own LDS
-// buffer (one of the ring's stage buffers) in two halves of 64 rows and writes whole 16-byte
-// chunks of output rows; only a chunk that crosses valid_n falls back to
-// element stores. The K loop's last barrier has released the LDS.
-__device__ __forceinline__ void store_tile(const v16f (&acc)[4][4], const TileSpec& ts, uint8_t* lds) {
+// Epilogue: each wave stages its 128 x 128 float sub-tile through its own
+// LDS area in four passes of one MFMA block row (32 rows), row pitch 136
+// floats (rows 4 apart, written by the two lane halves of a ds_write_b32,
+// then start 32 banks apart). It reads back 16-byte chunks: lane l takes
+// row 2 m + (l >> 5), columns 4 (l & 31) .. + 3, so a store instruction
+// writes two whole 128-column rows. Full tiles take a path without bounds
+// checks; edge tiles check rows and columns.
+constexpr int kEpiPitch = 136;
+constexpr int kEpiWaveBytes = 32 * kEpiPitch * 4;   // one wave's staging area
+
+template <bool F32>
+__device__ __forceinline__ void store_chunk(uint8_t* dst, const float4& v) {
+  if constexpr (F32)
+    *reinterpret_cast<float4*>(dst) = v;
+  else
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+}
+
+template <bool F32>
+__device__ __forceinline__ void store_tile_t(const v16f (&acc)[4][4], const TileSpec& ts, float* buf) {
+  constexpr int esz = F32 ? 4 : 2;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
-  float* buf = reinterpret_cast<float*>(lds);   // this wave's [64][128 + 4 pad]
-  const int esz = ts.out_f32 ? 4 : 2;
+  const bool full = ts.valid_m == kBM && ts.valid_n == kBN;
+  const int64_t rs = ts.ldo * esz;   // bytes per output row
+  const int lrow = lane >> 5, col = 4 * (lane & 31);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ts.out) + (int64_t)(wm * 128 + lrow) * rs + (wn * 128 + col) * esz;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int i = 2 * half + ii;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const int r = 32 * ii + 8 * (k >> 2) + 4 * (lane >> 5) + (k & 3);
-          buf[r * 132 + 32 * j + (lane & 31)] = acc[i][j][k];
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
+      for (int k = 0; k < 16; ++k)
+        buf[(8 * (k >> 2) + 4 * (lane >> 5) + (k & 3)) * kEpiPitch + 32 * j + (lane & 31)] = acc[i][j][k];
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
-    // 64 rows x 128 columns; a lane handles 4 consecutive columns per step
-    const int row0 = wm * 128 + 64 * half;
-    const int col0 = wn * 128;
-#pragma unroll 4
-    for (int e = lane; e < 64 * 32; e += 64) {
-      const int r = e >> 5, c = (e & 31) * 4;
-      const int row = row0 + r, col = col0 + c;
-      if (row >= ts.valid_m || col >= ts.valid_n) continue;
-      const float4 v = *reinterpret_cast<const float4*>(&buf[r * 132 + c]);
-      uint8_t* dst = reinterpret_cast<uint8_t*>(ts.out) + ((int64_t)row * ts.ldo + col) * esz;
-      if (col + 4 <= ts.valid_n) {
-        if (ts.out_f32)
-          *reinterpret_cast<float4*>(dst) = v;
-        else
-          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-      } else {
-        const float f[4] = {v.x, v.y, v.z, v.w};
-        for (int q = 0; q < ts.valid_n - col; ++q) {
-          if (ts.out_f32)
-            reinterpret_cast<float*>(dst)[q] = f[q];
-          else
-            reinterpret_cast<uint16_t*>(dst)[q] = (uint16_t)f32_to_bf16(f[q]);
+    uint8_t* rowp = base + (int64_t)(32 * i) * rs;
+    if (full) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m)
+        store_chunk<F32>(rowp + (int64_t)(2 * m) * rs,
+                         *reinterpret_cast<const float4*>(&buf[(2 * m + lrow) * kEpiPitch + col]));
+    } else {
+      const int grow0 = wm * 128 + 32 * i + lrow, gcol = wn * 128 + col;
+      for (int m = 0; m < 16; ++m) {
+        if (grow0 + 2 * m >= ts.valid_m || gcol >= ts.valid_n) continue;
+        const float4 v = *reinterpret_cast<const float4*>(&buf[(2 * m + lrow) * kEpiPitch + col]);
+        uint8_t* dst = rowp + (int64_t)(2 * m) * rs;
+        if (gcol + 4 <= ts.valid_n) {
+          store_chunk<F32>(dst, v);
+        } else {
+          const float f[4] = {v.x, v.y, v.z, v.w};
+          for (int q = 0; q < ts.valid_n - gcol; ++q) {
+            if constexpr (F32)
+              reinterpret_cast<float*>(dst)[q] = f[q];
+            else
+              reinterpret_cast<uint16_t*>(dst)[q] = (uint16_t)f32_to_bf16(f[q]);
+          }
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // the reads are done before the next pass writes
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+__device__ __forceinline__ void store_tile(const v16f (&acc)[4][4], const TileSpec& ts, uint8_t* lds) {
+  float* buf = reinterpret_cast<float*>(lds);
+  if (ts.out_f32)
+    store_tile_t<true>(acc, ts, buf);
+  else
+    store_tile_t<false>(acc, ts, buf);
 }
 
 // Writes zeros over a valid_m x valid_n tile (tail rows, empty groups).
@@ -401,7 +422,7 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& ts) {
   if (ks < nk) step_full(d, ks, nk, st0, st1, r, acc, wm, wn, lane, sink);
   MX_WAIT_VM_LDS(0);
   wg_barrier();   // every wave is done with the stage buffers
-  uint8_t* mine = (w & 1 ? st1 : st0) + (w >> 1) * (64 * 132 * 4);
+  uint8_t* mine = (w & 1 ? st1 : st0) + (w >> 1) * kEpiWaveBytes;
   store_tile(acc, ts, mine);
 }
 
@@ -425,6 +446,7 @@ constexpr int kHpT = 64;                  // tokens per K step
 constexpr int kHpRowB = 512;              // LDS bytes per token row (256 columns)
 constexpr int kHpPart = kHpT * kHpRowB;   // 32 KB per operand and stage
 static_assert(2 * kHpPart <= kStageBytes, "an hp stage fits a stage buffer");
+static_assert(2 * kEpiWaveBytes <= kStageBytes, "two waves' epilogue areas fit a stage buffer");
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -574,7 +596,7 @@ __device__ __forceinline__ void gemm_tile_hp(const TileSpec& ts) {
   if (ks < nk) step_hp(d, ks, nk, hs0, hs1, r, acc, wm, wn, lane);
   MX_WAIT_VM_LDS(0);
   wg_barrier();
-  uint8_t* mine = (w & 1 ? hs1 : hs0) + (w >> 1) * (64 * 132 * 4);
+  uint8_t* mine = (w & 1 ? hs1 : hs0) + (w >> 1) * kEpiWaveBytes;
   store_tile(acc, ts, mine);
 }
 
