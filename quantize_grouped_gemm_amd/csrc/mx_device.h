@@ -22,16 +22,16 @@ constexpr int kBlock = 32;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// float32 -> bf16 bits, round to nearest even; NaN -> 0x7FC0 with its sign.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-  return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? (((u >> 16) & 0x8000u) | 0x7FC0u) : r;
-}
+// float32 -> bf16 bits with gfx950's v_cvt_pk_bf16_f32: round to nearest
+// even (denormals kept), NaN stays a quiet NaN of the same sign.
+typedef __bf16 mx_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float mx_f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((mx_f32x2{lo, hi}), mx_bf16x2));
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.0f) & 0xFFFFu; }
 
 // max |v| over the 8 bf16 values of a 16-byte chunk, as 15-bit magnitude bits
 // (non-negative bf16 bit patterns order like their values; NaN > 0x7F80).

@@ -161,6 +161,73 @@ __device__ __forceinline__ void store_tile_t(const v16f (&acc)[4][4], const Tile
   }
 }
 
+// The tile's pointers are uniform over the workgroup but may be derived from
+// LDS values (group tables); reading them from lane 0 keeps buffer resources
+// in scalar registers.
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Epilogue of a full tile straight from the accumulators (no LDS). Lane l's
+// element (i, j, k) is row 32 i + 8 (k >> 2) + 4 h + (k & 3), column
+// 32 j + (l & 31) of its wave's sub-tile (h = l >> 5). The row part of each
+// store's offset is uniform (scalar offset), the lane part a vector offset.
+//   fp32: one dword store per element register: lanes 0..31 and 32..63 each
+//         write one whole 128-byte row segment.
+//   bf16: neighbouring lanes swap one value so that an even lane holds
+//         columns c, c + 1 of row r(k) and an odd lane columns c - 1, c of
+//         row r(k + 1); one dword store per register pair writes four
+//         64-byte row segments.
+// The caller guarantees 256 x 256 valid elements and 256 rows < 2^31 bytes.
+template <bool F32>
+__device__ __forceinline__ void store_tile_direct(const v16f (&acc)[4][4], const TileSpec& ts) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int h = lane >> 5, c = lane & 31;
+  const uint32_t rs = (uint32_t)ts.ldo * (F32 ? 4u : 2u);   // row pitch in bytes
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(ts.out), (short)0, 0x7FFFFFFF, 0x00020000);
+  if constexpr (F32) {
+    const uint32_t voff = (uint32_t)(wm * 128 + 4 * h) * rs + (uint32_t)(wn * 128 + c) * 4u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t soff = (uint32_t)(32 * i + 8 * (k >> 2) + (k & 3)) * rs;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][k]), r, voff + 128u * j, soff, 0);
+      }
+  } else {
+    // selections by mask arithmetic: the registers are indexed statically
+    const uint32_t om = 0u - (uint32_t)(lane & 1);   // all ones on odd lanes
+    const uint32_t voff = (uint32_t)(wm * 128 + 4 * h + (lane & 1)) * rs + (uint32_t)(wn * 128 + (c & ~1)) * 2u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t soff = (uint32_t)(32 * i + 8 * (q >> 1) + 2 * (q & 1)) * rs;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t u0 = __float_as_uint(acc[i][j][2 * q]), u1 = __float_as_uint(acc[i][j][2 * q + 1]);
+          const uint32_t send = u1 ^ ((u0 ^ u1) & om);   // even lanes send row k + 1, odd lanes row k
+          const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true);
+          const uint32_t lo = u0 ^ ((u0 ^ got) & om);
+          const uint32_t hi = got ^ ((got ^ u1) & om);
+          __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(__uint_as_float(lo), __uint_as_float(hi)), r,
+                                                voff + 64u * j, soff, 0);
+        }
+      }
+  }
+}
+
+__device__ __forceinline__ bool direct_epilogue(const TileSpec& ts) {
+  return ts.valid_m == kBM && ts.valid_n == kBN && ts.ldo * (ts.out_f32 ? 4 : 2) * kBM < ((int64_t)1 << 31);
+}
+
 __device__ __forceinline__ void store_tile(const v16f (&acc)[4][4], const TileSpec& ts, uint8_t* lds) {
   float* buf = reinterpret_cast<float*>(lds);
   if (ts.out_f32)
@@ -421,6 +488,13 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& ts) {
   }
   if (ks < nk) step_full(d, ks, nk, st0, st1, r, acc, wm, wn, lane, sink);
   MX_WAIT_VM_LDS(0);
+  if (direct_epilogue(ts)) {
+    if (ts.out_f32)
+      store_tile_direct<true>(acc, ts);
+    else
+      store_tile_direct<false>(acc, ts);
+    return;
+  }
   wg_barrier();   // every wave is done with the stage buffers
   uint8_t* mine = (w & 1 ? st1 : st0) + (w >> 1) * kEpiWaveBytes;
   store_tile(acc, ts, mine);
@@ -595,6 +669,13 @@ __device__ __forceinline__ void gemm_tile_hp(const TileSpec& ts) {
   }
   if (ks < nk) step_hp(d, ks, nk, hs0, hs1, r, acc, wm, wn, lane);
   MX_WAIT_VM_LDS(0);
+  if (direct_epilogue(ts)) {
+    if (ts.out_f32)
+      store_tile_direct<true>(acc, ts);
+    else
+      store_tile_direct<false>(acc, ts);
+    return;
+  }
   wg_barrier();
   uint8_t* mine = (w & 1 ? hs1 : hs0) + (w >> 1) * kEpiWaveBytes;
   store_tile(acc, ts, mine);
