@@ -819,11 +819,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
     if (lane == 0) ends[a.E] = (int32_t)a.M;
   }
   __syncthreads();
-  const int mt = tile_end[a.E];
+  const int mt = tile_end[a.E];            // row tiles, the tail's included
+  const int mt_groups = tile_end[a.E - 1]; // row tiles of the groups
   const int nt = (int)((a.N + kBN - 1) / kBN);
-  if ((int)blockIdx.x >= mt * nt) return;
+  const int b = (int)blockIdx.x;
+  if (b >= mt * nt) return;
+  // the groups' tiles are dealt to the XCDs in equal contiguous runs; the
+  // tail's zero tiles come after them, so no XCD's run is padded with them
   int tile, tn, bfirst, brows;
-  band_order(xcd_remap(blockIdx.x, mt * nt), mt, nt, tile, tn, bfirst, brows);
+  if (b < mt_groups * nt) {
+    band_order(xcd_remap(b, mt_groups * nt), mt_groups, nt, tile, tn, bfirst, brows);
+  } else {
+    const int z = b - mt_groups * nt;
+    tile = mt_groups + z / nt;
+    tn = z % nt;
+    bfirst = tile;
+    brows = 1;
+  }
   // first group whose row-tile range ends past `tile`
   int lo = 0, hi = a.E;
   while (lo < hi) {
