@@ -171,6 +171,45 @@ __device__ __forceinline__ void* uniform_ptr(const void* p) {
   return (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int uniform_i32(int v) { return (int)__builtin_amdgcn_readfirstlane((uint32_t)v); }
+
+// Every field of a tile is the same in all lanes of the workgroup, but the
+// grouped kernels derive them from group tables in LDS, which the compiler
+// treats as per-lane values: buffer resources built from them would then be
+// wrapped in a loop over distinct lane values at every DMA. Reading each
+// field from lane 0 keeps them in scalar registers.
+__device__ __forceinline__ TileSpec uniform_spec(const TileSpec& t) {
+  TileSpec u;
+  u.a = (const uint8_t*)uniform_ptr(t.a);
+  u.sa = (const uint8_t*)uniform_ptr(t.sa);
+  u.b = (const uint8_t*)uniform_ptr(t.b);
+  u.sb = (const uint8_t*)uniform_ptr(t.sb);
+  u.lda = uniform_i64(t.lda);
+  u.ldb = uniform_i64(t.ldb);
+  u.sstep_a = uniform_i64(t.sstep_a);
+  u.sstep_b = uniform_i64(t.sstep_b);
+  u.sbytes_a = uniform_i64(t.sbytes_a);
+  u.sbytes_b = uniform_i64(t.sbytes_b);
+  u.valid_m = uniform_i32(t.valid_m);
+  u.valid_n = uniform_i32(t.valid_n);
+  u.k_begin = uniform_i64(t.k_begin);
+  u.nk = uniform_i32(t.nk);
+  u.pf_a0 = uniform_i32(t.pf_a0);
+  u.pf_an = uniform_i32(t.pf_an);
+  u.pf_b0 = uniform_i32(t.pf_b0);
+  u.pf_bn = uniform_i32(t.pf_bn);
+  u.out = uniform_ptr(t.out);
+  u.ldo = uniform_i64(t.ldo);
+  u.out_f32 = uniform_i32(t.out_f32) != 0;
+  return u;
+}
+
 // Epilogue of a full tile straight from the accumulators (no LDS). Lane l's
 // element (i, j, k) is row 32 i + 8 (k >> 2) + 4 h + (k & 3), column
 // 32 j + (l & 31) of its wave's sub-tile (h = l >> 5). The row part of each
@@ -422,7 +461,8 @@ __device__ __forceinline__ void step_full(const TileDma& d, int ks, int nk, uint
   }
 }
 
-__device__ __forceinline__ void gemm_tile(const TileSpec& ts) {
+__device__ __forceinline__ void gemm_tile(const TileSpec& tile) {
+  const TileSpec ts = uniform_spec(tile);
   __shared__ __align__(16) uint8_t st0[kStageBytes];
   __shared__ __align__(16) uint8_t st1[kStageBytes];
   __shared__ __align__(16) uint8_t sink[256];
@@ -622,7 +662,8 @@ __device__ __forceinline__ void step_hp(const HpDma& d, int ks, int nk, uint8_t*
 // ts.a / ts.b: column n0 of G / k0 of X (token row 0); ts.lda / ts.ldb: bytes
 // per token row; ts.sbytes_a / sbytes_b: bytes from ts.a / ts.b to the end
 // of the operand; ts.k_begin: first token; ts.nk: 64-token steps (even).
-__device__ __forceinline__ void gemm_tile_hp(const TileSpec& ts) {
+__device__ __forceinline__ void gemm_tile_hp(const TileSpec& tile) {
+  const TileSpec ts = uniform_spec(tile);
   __shared__ __align__(16) uint8_t hs0[kStageBytes];
   __shared__ __align__(16) uint8_t hs1[kStageBytes];
   if (ts.nk <= 0) {
