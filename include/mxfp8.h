@@ -251,6 +251,28 @@ mx_status mx_pad_groups(const void* x, const int32_t* group_sizes, int32_t E,
                         int64_t Tcap, void* x_pad, int32_t* offs_pad,
                         int32_t* src_row, int32_t* dev_err, void* stream);
 
+/* Per-group padding fused with MX quantization: the result equals
+ * mx_pad_groups (row_bytes = 2 * cols) followed by mx_quantize of the bf16
+ * x_pad [Tcap, cols], but x_pad is never written. The padded layout is what
+ * the grouped GEMMs consume ([P3], The integration: the dispatcher hands the
+ * kernels a padded expert-major layout, pad_multiple=128; [P1], the
+ * torchtitan commit on dynamic per-group padding kernels); writing it
+ * straight in MXFP8 is this library's fusion of those two steps.
+ * x: bf16 [T, cols] row-major, tokens grouped by expert in expert order.
+ * group_sizes: device int32 [E]. Outputs as mx_quantize writes them for
+ * [Tcap, cols] (pad rows and the tail quantize to code 0x00 with scale
+ * 0x00), plus offs_pad [E] and src_row [Tcap] as mx_pad_groups writes them.
+ * cols % 32 == 0 (% 128 for K128 row-wise scales); column-wise output needs
+ * Tcap % 32 == 0 (% 128 for K128). Size errors are reported in *dev_err as
+ * by mx_pad_groups. Two kernels are enqueued on `stream`. */
+mx_status mx_pad_quantize(const void* x, const int32_t* group_sizes, int32_t E,
+                          int64_t T, int64_t cols, int32_t pad_multiple,
+                          int64_t Tcap, mx_scale_mode mode, unsigned dirs,
+                          mx_scale_layout layout, uint8_t* q_row,
+                          uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                          int32_t* offs_pad, int32_t* src_row,
+                          int32_t* dev_err, void* stream);
+
 /* Inverse of mx_pad_groups: y[src_row[r]] = y_pad[r] for every padded row r
  * with 0 <= src_row[r] < T. y_pad [Tcap, row_bytes], y [T, row_bytes]. Rows
  * of y that no padded row maps to are left untouched. */

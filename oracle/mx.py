@@ -414,6 +414,16 @@ def pad_groups(x_bits, sizes, multiple, Tcap):
     return x_pad, offs.astype(np.int32), src_row
 
 
+def pad_quantize(x_bits, sizes, multiple, Tcap, mode, rowwise=True, colwise=False):
+    """Padding followed by MX quantization of the padded bf16 tensor: what a
+    fused pad + quantize must produce. Composition of pad_groups and
+    quantize_bf16; the dict also holds 'offs' and 'src_row'."""
+    x_pad, offs, src_row = pad_groups(x_bits, sizes, multiple, Tcap)
+    out = quantize_bf16(x_pad, mode, rowwise, colwise)
+    out["offs"], out["src_row"] = offs, src_row
+    return out
+
+
 def unpad_groups(y_pad, src_row, T):
     """Inverse of pad_groups: y[src_row[r]] = y_pad[r] for every real row."""
     y_pad = np.asarray(y_pad)

@@ -322,6 +322,49 @@ mx_status mx_pad_groups(const void* x, const int32_t* group_sizes, int32_t E, in
   return launched(mxk::launch_pad(a, as_stream(stream)), fn);
 }
 
+mx_status mx_pad_quantize(const void* x, const int32_t* group_sizes, int32_t E, int64_t T, int64_t cols,
+                          int32_t pad_multiple, int64_t Tcap, mx_scale_mode mode, unsigned dirs,
+                          mx_scale_layout layout, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                          int32_t* offs_pad, int32_t* src_row, int32_t* dev_err, void* stream) {
+  const char* fn = "mx_pad_quantize";
+  MX_REQUIRE(mode == MX_RCEIL || mode == MX_FLOOR, MX_ERR_ARG, "%s: bad scale mode %d", fn, (int)mode);
+  MX_REQUIRE(dirs != 0 && (dirs & ~3u) == 0, MX_ERR_ARG, "%s: dirs must be MX_ROWWISE|MX_COLWISE", fn);
+  MX_REQUIRE(layout == MX_SCALES_PLAIN || layout == MX_SCALES_K128, MX_ERR_ARG, "%s: bad scale layout", fn);
+  const bool k128 = layout == MX_SCALES_K128;
+  MX_REQUIRE(E >= 1 && E <= 1024, MX_ERR_SHAPE, "%s: E must be in [1, 1024]", fn);
+  MX_REQUIRE(T >= 0 && Tcap >= 0 && T < (1ll << 31) && Tcap < (1ll << 31), MX_ERR_SHAPE, "%s: T/Tcap out of range", fn);
+  MX_REQUIRE(cols > 0 && cols % 32 == 0, MX_ERR_SHAPE, "%s: cols (%lld) must be a positive multiple of 32", fn,
+             (long long)cols);
+  MX_REQUIRE(pad_multiple > 0 && pad_multiple % 32 == 0, MX_ERR_SHAPE,
+             "%s: pad_multiple must be a positive multiple of 32", fn);
+  MX_REQUIRE(!k128 || !(dirs & MX_ROWWISE) || cols % 128 == 0, MX_ERR_SHAPE,
+             "%s: K128 row-wise scales need cols (%lld) to be a multiple of 128", fn, (long long)cols);
+  MX_REQUIRE(!(dirs & MX_COLWISE) || Tcap % (k128 ? 128 : 32) == 0, MX_ERR_SHAPE,
+             "%s: column-wise output needs Tcap (%lld) to be a multiple of %d", fn, (long long)Tcap, k128 ? 128 : 32);
+  MX_REQUIRE((Tcap + 127) / 128 <= 65535, MX_ERR_SHAPE, "%s: Tcap too large for one launch", fn);
+  MX_REQUIRE(group_sizes && offs_pad && (Tcap == 0 || src_row) && (T == 0 || x), MX_ERR_NULL, "%s: NULL pointer", fn);
+  MX_REQUIRE(T == 0 || al16(x), MX_ERR_ALIGN, "%s: x must be 16-byte aligned", fn);
+  if (Tcap > 0 && (dirs & MX_ROWWISE)) {
+    MX_REQUIRE(q_row && s_row, MX_ERR_NULL, "%s: q_row/s_row NULL", fn);
+    MX_REQUIRE(al16(q_row) && (!k128 || al4(s_row)), MX_ERR_ALIGN, "%s: q_row must be 16-byte and K128 s_row 4-byte aligned", fn);
+  }
+  if (Tcap > 0 && (dirs & MX_COLWISE)) {
+    MX_REQUIRE(q_col && s_col, MX_ERR_NULL, "%s: q_col/s_col NULL", fn);
+    MX_REQUIRE(al16(q_col) && (!k128 || al4(s_col)), MX_ERR_ALIGN, "%s: q_col must be 16-byte and K128 s_col 4-byte aligned", fn);
+  }
+  MX_DEVICE();
+  hipStream_t st = as_stream(stream);
+  mxk::PadArgs p{static_cast<const uint8_t*>(x), group_sizes, E, T, cols * 2, Tcap, pad_multiple, nullptr,
+                 offs_pad, src_row, dev_err};
+  mx_status r = launched(mxk::launch_pad_map(p, st), fn);
+  if (r != MX_OK || Tcap == 0) return r;
+  mxk::QuantArgs a{static_cast<const uint16_t*>(x), Tcap, cols, cols, mode == MX_RCEIL, k128,
+                   (dirs & MX_ROWWISE) ? q_row : nullptr, (dirs & MX_ROWWISE) ? s_row : nullptr,
+                   (dirs & MX_COLWISE) ? q_col : nullptr, (dirs & MX_COLWISE) ? s_col : nullptr,
+                   src_row, T};
+  return launched(mxk::launch_quant(a, 1, st), fn);
+}
+
 mx_status mx_unpad_groups(const void* y_pad, const int32_t* src_row, int64_t Tcap, int64_t T, int64_t row_bytes,
                           void* y, void* stream) {
   const char* fn = "mx_unpad_groups";

@@ -15,6 +15,10 @@ struct QuantArgs {
   int64_t rows, cols, ld;
   bool rceil, k128;
   uint8_t *q_row, *s_row, *q_col, *s_col;
+  // optional row gather (one matrix only): output row r quantizes input row
+  // src_row[r] of x, or zeros where src_row[r] is negative or >= src_rows
+  const int32_t* src_row = nullptr;
+  int64_t src_rows = 0;
 };
 
 struct SwigluFwdArgs {
@@ -89,6 +93,7 @@ hipError_t launch_gemm_wgrad(const GemmArgs& a, hipStream_t s);
 // lda / ldb their row pitches in bytes, out bf16 [E, N, K].
 hipError_t launch_gemm_wgrad_hp(const GemmArgs& a, hipStream_t s);
 hipError_t launch_pad(const PadArgs& a, hipStream_t s);
+hipError_t launch_pad_map(const PadArgs& a, hipStream_t s);   // offs_pad and src_row only
 hipError_t launch_unpad(const UnpadArgs& a, hipStream_t s);
 
 }  // namespace mxk

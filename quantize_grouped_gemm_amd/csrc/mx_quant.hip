@@ -181,6 +181,23 @@ __device__ __forceinline__ void tile_load(uint4 (&v)[kTileChunks], const uint16_
   }
 }
 
+// tile_load through a row map: tile row `row` reads input row
+// src_row[r0 + row], or zeros where that is negative or past src_rows.
+__device__ __forceinline__ void tile_load_gather(uint4 (&v)[kTileChunks], const uint16_t* x, int64_t ld,
+                                                 const int32_t* src_row, int64_t src_rows, int64_t r0,
+                                                 int64_t c0, int rows_valid, int cols_valid) {
+  const int t = threadIdx.x;
+  const int cc = t & 15;
+#pragma unroll
+  for (int j = 0; j < kTileChunks; ++j) {
+    const int row = (t >> 4) + 16 * j;
+    const int64_t src = row < rows_valid ? (int64_t)src_row[r0 + row] : -1;
+    v[j] = (src >= 0 && src < src_rows && cc * 8 < cols_valid)
+               ? *reinterpret_cast<const uint4*>(x + src * ld + c0 + cc * 8)
+               : make_uint4(0, 0, 0, 0);
+  }
+}
+
 __device__ __forceinline__ void tile_store_bf16(const uint4 (&v)[kTileChunks], uint16_t* base,
                                                 int64_t ld, int rows_valid, int cols_valid) {
   const int t = threadIdx.x;
@@ -205,7 +222,10 @@ __global__ __launch_bounds__(kTileThreads) void k_quant_tile(QuantArgs a) {
   const int rows_valid = (int)min<int64_t>(kTR, a.rows - r0);
   const int cols_valid = (int)min<int64_t>(kTC, a.cols - c0);
   uint4 v[kTileChunks];
-  tile_load(v, a.x + (bz * a.rows + r0) * a.ld + c0, a.ld, rows_valid, cols_valid);
+  if (a.src_row)
+    tile_load_gather(v, a.x, a.ld, a.src_row, a.src_rows, r0, c0, rows_valid, cols_valid);
+  else
+    tile_load(v, a.x + (bz * a.rows + r0) * a.ld + c0, a.ld, rows_valid, cols_valid);
   if (a.q_row) {
     TileOut o{a.q_row + bz * a.rows * a.cols, a.s_row + bz * a.rows * (a.cols / kBlock), a.cols, a.rows, a.k128};
     tile_rowq(v, rows_valid, cols_valid, a.rceil, o, r0, c0);

@@ -19,7 +19,10 @@ quoted on the TrainingWeightWrapperTensor page):
             dx   = dZ w13                     (w13 quantized along 2H)
             dW13 = dZ^T x
 The grouped variant pads each expert's tokens to a multiple of 128 first,
-runs the grouped GEMMs over the padded offsets and unpads y and dx.
+runs the grouped GEMMs over the padded offsets and unpads y and dx. With the
+MXFP8 weight gradient the padding of x and dy is fused into their
+quantization (no bf16 padded copy); the hp recipe keeps the bf16 copies,
+which its weight-gradient GEMM reads.
 
 Every buffer is allocated once per shape by the workspace classes, so a
 training step only enqueues kernels. The weight-gradient GEMMs run in MXFP8
@@ -43,6 +46,13 @@ def _qbytes(n, dual):
     """Bytes a quantization of n bf16 values must move: read 2, write 1 code
     + 1/32 scale per direction."""
     return n * (2 + (2 if dual else 1) * (1 + 1 / 32))
+
+
+def _pad_qbytes(T, Tcap, D):
+    """Bytes of the fused pad + dual quantization: the T real rows are read
+    once, the padded [Tcap, D] codes and scales are written both ways, and the
+    row map is written."""
+    return 2 * T * D + Tcap * D * 2 * (1 + 1 / 32) + 4 * Tcap
 
 
 def _q_out(lead, R, C, dev, row=True, col=True):
@@ -136,8 +146,10 @@ class MoEMLP:
         dev = device
         bf = torch.bfloat16
         mxw = wgrad == "mx"
-        self.x_pad = torch.empty((Tcap, D), dtype=bf, device=dev)
-        self.dy_pad = torch.empty((Tcap, D), dtype=bf, device=dev)
+        # bf16 padded copies exist only for the hp weight gradient; the MXFP8
+        # recipe pads while it quantizes
+        self.x_pad = None if mxw else torch.empty((Tcap, D), dtype=bf, device=dev)
+        self.dy_pad = None if mxw else torch.empty((Tcap, D), dtype=bf, device=dev)
         self.offs = torch.empty((E,), dtype=torch.int32, device=dev)
         self.src = torch.empty((Tcap,), dtype=torch.int32, device=dev)
         self.offs2 = torch.empty((E,), dtype=torch.int32, device=dev)
@@ -177,13 +189,20 @@ class MoEMLP:
         mxw = self.wgrad == "mx"
         z0, z1 = self.z[:, :H], self.z[:, H:]
         err = self.err
-        st = [
-            Stage("pad_x", "k_pad", 0, 2 * T * D + 2 * Tc * D,
-                  lambda: mx.pad_groups(x, sizes, Tc, self.multiple,
-                                        out=dict(x_pad=self.x_pad, offs=self.offs, src_row=self.src),
-                                        dev_err=err)),
-            Stage("quant_x", "k_quant_tile", 0, _qbytes(Tc * D, mxw),
-                  lambda: mx.quantize(self.x_pad, m, True, mxw, out=self.qx)),
+        if mxw:
+            # padding fused into the dual quantization (k_pad_map + k_quant_tile)
+            st = [Stage("pad_quant_x", "k_quant_tile", 0, _pad_qbytes(T, Tc, D),
+                        lambda: mx.pad_quantize(x, sizes, Tc, m, True, True, multiple=self.multiple,
+                                                out=dict(self.qx, offs=self.offs, src_row=self.src),
+                                                dev_err=err))]
+        else:
+            st = [Stage("pad_x", "k_pad", 0, 2 * T * D + 2 * Tc * D,
+                        lambda: mx.pad_groups(x, sizes, Tc, self.multiple,
+                                              out=dict(x_pad=self.x_pad, offs=self.offs, src_row=self.src),
+                                              dev_err=err)),
+                  Stage("quant_x", "k_quant_tile", 0, _qbytes(Tc * D, False),
+                        lambda: mx.quantize(self.x_pad, m, True, False, out=self.qx))]
+        st += [
             Stage("quant_w13", "k_quant_tile", 0, _qbytes(E * 2 * H * D, True),
                   lambda: mx.quantize(w13, m, True, True, out=self.q13)),
             Stage("quant_w2", "k_quant_tile", 0, _qbytes(E * D * H, True),
@@ -198,12 +217,20 @@ class MoEMLP:
                                             self.q2["s_row"], self.offs, out=self.y_pad, dev_err=err)),
             Stage("unpad_y", "k_unpad", 0, 4 * T * D,
                   lambda: mx.unpad_groups(self.y_pad, self.src, T, out=self.y)),
-            Stage("pad_dy", "k_pad", 0, 2 * T * D + 2 * Tc * D,
-                  lambda: mx.pad_groups(dy, sizes, Tc, self.multiple,
-                                        out=dict(x_pad=self.dy_pad, offs=self.offs2, src_row=self.src2),
-                                        dev_err=err)),
-            Stage("quant_dy", "k_quant_tile", 0, _qbytes(Tc * D, mxw),
-                  lambda: mx.quantize(self.dy_pad, m, True, mxw, out=self.qdy)),
+        ]
+        if mxw:
+            st.append(Stage("pad_quant_dy", "k_quant_tile", 0, _pad_qbytes(T, Tc, D),
+                            lambda: mx.pad_quantize(dy, sizes, Tc, m, True, True, multiple=self.multiple,
+                                                    out=dict(self.qdy, offs=self.offs2, src_row=self.src2),
+                                                    dev_err=err)))
+        else:
+            st += [Stage("pad_dy", "k_pad", 0, 2 * T * D + 2 * Tc * D,
+                         lambda: mx.pad_groups(dy, sizes, Tc, self.multiple,
+                                               out=dict(x_pad=self.dy_pad, offs=self.offs2, src_row=self.src2),
+                                               dev_err=err)),
+                   Stage("quant_dy", "k_quant_tile", 0, _qbytes(Tc * D, False),
+                         lambda: mx.quantize(self.dy_pad, m, True, False, out=self.qdy))]
+        st += [
             Stage("gemm_w2_dgrad", "k_gemm_grouped", 2 * T * D * H, 0,
                   lambda: mx.grouped_mm_dgrad(self.qdy["q_row"], self.qdy["s_row"], self.q2["q_col"],
                                               self.q2["s_col"], self.offs, out=self.dh, dev_err=err)),

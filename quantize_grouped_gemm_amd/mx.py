@@ -48,6 +48,8 @@ _SIGS = {
                                    ctypes.c_int),
     "mx_grouped_mm_wgrad_hp": ([_P, _P, _P, _I32, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "mx_pad_groups": ([_P, _P, _I32, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
+    "mx_pad_quantize": ([_P, _P, _I32, _I64, _I64, _I32, _I64, ctypes.c_int, ctypes.c_uint, ctypes.c_int, _P, _P,
+                         _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "mx_unpad_groups": ([_P, _P, _I64, _I64, _I64, _P, _P], ctypes.c_int),
 }
 EXPORTS = tuple(_SIGS)
@@ -254,6 +256,38 @@ def pad_groups(x, sizes, Tcap, multiple=128, out=None, dev_err=None):
                              _ptr(offs), _ptr(src), _ptr(dev_err), _stream(dev))
     _check(st, "mx_pad_groups")
     return x_pad, offs, src
+
+
+def pad_quantize(x, sizes, Tcap, mode="rceil", rowwise=True, colwise=False, layout="k128", multiple=128,
+                 out=None, dev_err=None):
+    """Padding fused with MX quantization: the outputs of
+    quantize(pad_groups(x, sizes, Tcap)[0]) without the bf16 x_pad.
+
+    x bf16 [T, C] contiguous; sizes int32 [E] on the device. Returns dict with
+    q_row/s_row and/or q_col/s_col of the padded [Tcap, C] tensor, plus offs
+    int32 [E] and src_row int32 [Tcap]."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous()
+    T, C = x.shape
+    E = sizes.shape[0]
+    dev = x.device
+    out = dict(out or {})
+    if rowwise:
+        out.setdefault("q_row", _u8((Tcap, C), dev))
+        out.setdefault("s_row", _u8(scale_shape(Tcap, C, layout), dev))
+    if colwise:
+        out.setdefault("q_col", _u8((C, Tcap), dev))
+        out.setdefault("s_col", _u8(scale_shape(C, Tcap, layout), dev))
+    if out.get("offs") is None:
+        out["offs"] = torch.empty((E,), dtype=torch.int32, device=dev)
+    if out.get("src_row") is None:
+        out["src_row"] = torch.empty((Tcap,), dtype=torch.int32, device=dev)
+    dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
+    st = lib().mx_pad_quantize(_ptr(x), _ptr(sizes), E, T, C, multiple, Tcap, _MODES[mode], dirs,
+                               _LAYOUTS[layout], _ptr(out.get("q_row")), _ptr(out.get("s_row")),
+                               _ptr(out.get("q_col")), _ptr(out.get("s_col")), _ptr(out["offs"]),
+                               _ptr(out["src_row"]), _ptr(dev_err), _stream(dev))
+    _check(st, "mx_pad_quantize")
+    return out
 
 
 def unpad_groups(y_pad, src_row, T, out=None):

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from _helpers import bf16_host, dev, host, to_dev
+from _helpers import bf16_host, dev, host, plain, to_dev
 from oracle import mx as O
 from quantize_grouped_gemm_amd import mlp, mx, synth
 
@@ -32,6 +32,52 @@ def test_pad_unpad(gpu, sizes):
     y = torch.full((T, 96), 7.0, dtype=torch.bfloat16, device=dev())
     mx.unpad_groups(x_pad, src, T, out=y)
     np.testing.assert_array_equal(bf16_host(y), xb)
+
+
+@pytest.mark.parametrize("layout", ["plain", "k128"])
+@pytest.mark.parametrize("sizes,D", [([3, 0, 130, 1], 128), ([128, 128], 256), ([0, 0, 5], 128), ([0], 128),
+                                     ([700, 0, 0, 300, 129], 384), ([257], 128)])
+def test_pad_quantize(gpu, sizes, D, layout):
+    """Fused pad + quantize: bytes equal the oracle's pad-then-quantize, and
+    offs / src_row equal the padding kernel's."""
+    sizes = np.array(sizes, np.int32)
+    T = int(sizes.sum())
+    Tcap = synth.capacity(T, len(sizes))
+    g = synth.generator(T + D)
+    xb = synth.bits(synth.normal_bf16((max(T, 1), D), 1.0, g))[:T]
+    xb[T // 2: T // 2 + 1, :32] = 0          # a zero block inside a group
+    x = to_dev(xb.view(np.int16)).view(torch.bfloat16) if T else torch.empty((0, D), dtype=torch.bfloat16,
+                                                                            device=dev())
+    for mode in ("rceil", "floor"):
+        for row, col in ((True, False), (False, True), (True, True)):
+            err = torch.zeros(1, dtype=torch.int32, device=dev())
+            got = mx.pad_quantize(x, to_dev(sizes), Tcap, mode, row, col, layout=layout, dev_err=err)
+            ref = O.pad_quantize(xb, sizes, 128, Tcap, mode, row, col)
+            np.testing.assert_array_equal(host(got["offs"]), ref["offs"])
+            np.testing.assert_array_equal(host(got["src_row"]), ref["src_row"])
+            for k in (["q_row", "s_row"] if row else []) + (["q_col", "s_col"] if col else []):
+                v = host(got[k])
+                if k[0] == "s" and layout == "k128":
+                    v = plain(v)
+                np.testing.assert_array_equal(v, ref[k], err_msg=f"{k} {mode}")
+            assert int(err.item()) == 0
+
+
+def test_pad_quantize_full_size_equals_unfused(gpu):
+    """At the MoE Scout shape (T=16384 tokens of dim 5120 over 16 experts),
+    the fused path writes the same bytes as padding then quantizing."""
+    E, T, D = 16, 16384, 5120
+    sizes = synth.zipf_group_sizes(T, E, 14).astype(np.int32)
+    Tcap = synth.capacity(T, E)
+    g = synth.generator(5, device=dev())
+    x = synth.normal_bf16((T, D), 1.0, g, device=dev())
+    sz = to_dev(sizes)
+    fused = mx.pad_quantize(x, sz, Tcap, "rceil", True, True)
+    x_pad, offs, src = mx.pad_groups(x, sz, Tcap)
+    ref = mx.quantize(x_pad, "rceil", True, True)
+    assert torch.equal(fused["offs"], offs) and torch.equal(fused["src_row"], src)
+    for k in ("q_row", "s_row", "q_col", "s_col"):
+        assert torch.equal(fused[k], ref[k]), k
 
 
 def test_pad_invalid_sizes_flag(gpu):

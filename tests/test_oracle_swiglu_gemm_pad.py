@@ -261,3 +261,29 @@ def test_pad_invariants_random_and_errors():
         mx.pad_groups(np.zeros((10, 4), np.uint16), np.array([5, 6]), 128, 256)
     with pytest.raises(ValueError):
         mx.pad_groups(np.zeros((300, 4), np.uint16), np.array([100, 100, 100]), 128, 256)
+
+
+def test_pad_quantize_is_rowwise_scatter_of_token_codes():
+    """Row-wise MX quantization is row-local, so the padded tensor's row-wise
+    codes are the tokens' own codes moved to their padded rows, and every pad
+    row is code 0x00 with scale 0x00 (amax 0). Column-wise blocks of a padded
+    tensor only ever see extra zeros, which leave each block's amax unchanged:
+    a column block of one group's real rows equals that block quantized with
+    the pad rows left out."""
+    rng = np.random.default_rng(7)
+    sizes = np.array([70, 0, 130, 1, 60])
+    T, D, Tcap = int(sizes.sum()), 64, 768
+    x = synth.bits(torch.from_numpy(rng.standard_normal((T, D))).to(torch.bfloat16))
+    for mode in ("rceil", "floor"):
+        got = mx.pad_quantize(x, sizes, 128, Tcap, mode, rowwise=True, colwise=True)
+        tok = mx.quantize_bf16(x, mode, rowwise=True)
+        src = got["src_row"]
+        real = src >= 0
+        np.testing.assert_array_equal(got["q_row"][real], tok["q_row"][src[real]])
+        np.testing.assert_array_equal(got["s_row"][real], tok["s_row"][src[real]])
+        assert np.all(got["q_row"][~real] == 0) and np.all(got["s_row"][~real] == 0)
+        # group 0 holds tokens 0..69 in padded rows 0..69: rows 0..63 form two
+        # whole column blocks of real tokens
+        blk = mx.quantize_bf16(x[:64], mode, rowwise=False, colwise=True)
+        np.testing.assert_array_equal(got["q_col"][:, :64], blk["q_col"])
+        np.testing.assert_array_equal(got["s_col"][:, :2], blk["s_col"])
