@@ -48,6 +48,16 @@ def _qbytes(n, dual):
     return n * (2 + (2 if dual else 1) * (1 + 1 / 32))
 
 
+_WEIGHT_STAGES = ("quant_w13", "quant_w2")
+
+
+def _weights_cached(stages, quantize_weights):
+    """Drops the weight quantizations when the cached MXFP8 weights are
+    reused: weights change only at the optimizer step, so the micro-batches
+    of one step can share one dual quantization of w13 and w2."""
+    return stages if quantize_weights else [st for st in stages if st.name not in _WEIGHT_STAGES]
+
+
 def _pad_qbytes(T, Tcap, D):
     """Bytes of the fused pad + dual quantization: the T real rows are read
     once, the padded [Tcap, D] codes and scales are written both ways, and the
@@ -87,14 +97,20 @@ class DenseMLP:
         self.dw2 = torch.empty((D, H), dtype=wgrad_dtype, device=dev)
         self.dw13 = torch.empty((2 * H, D), dtype=wgrad_dtype, device=dev)
 
-    def step(self, x, w13, w2, dy):
-        """One forward + backward; returns (dx, dW13, dW2)."""
-        for st in self.stages(x, w13, w2, dy):
+    def step(self, x, w13, w2, dy, quantize_weights=True):
+        """One forward + backward; returns (dx, dW13, dW2). With
+        quantize_weights=False the weights' MXFP8 copies from the previous
+        step are reused (valid while the weights are unchanged, i.e. between
+        optimizer steps)."""
+        for st in self.stages(x, w13, w2, dy, quantize_weights):
             st.fn()
         return self.dx, self.dw13, self.dw2
 
-    def stages(self, x, w13, w2, dy):
+    def stages(self, x, w13, w2, dy, quantize_weights=True):
         """The step as an ordered list of Stage (same calls as step())."""
+        return _weights_cached(self._stages(x, w13, w2, dy), quantize_weights)
+
+    def _stages(self, x, w13, w2, dy):
         T, D, H, m = self.T, self.D, self.H, self.mode
         z0, z1 = self.z[:, :H], self.z[:, H:]
         return [
@@ -175,16 +191,21 @@ class MoEMLP:
         self.dw2 = torch.empty((E, D, H), dtype=wdt, device=dev)
         self.dw13 = torch.empty((E, 2 * H, D), dtype=wdt, device=dev)
 
-    def step(self, x, sizes, w13, w2, dy):
-        """One forward + backward; returns (dx, dW13, dW2)."""
-        for st in self.stages(x, sizes, w13, w2, dy):
+    def step(self, x, sizes, w13, w2, dy, quantize_weights=True):
+        """One forward + backward; returns (dx, dW13, dW2). With
+        quantize_weights=False the experts' MXFP8 weight copies from the
+        previous step are reused (valid between optimizer steps)."""
+        for st in self.stages(x, sizes, w13, w2, dy, quantize_weights):
             st.fn()
         return self.dx, self.dw13, self.dw2
 
-    def stages(self, x, sizes, w13, w2, dy):
+    def stages(self, x, sizes, w13, w2, dy, quantize_weights=True):
         """The step as an ordered list of Stage (same calls as step()).
         GEMM flops count real tokens only; padded rows are executed but not
         counted."""
+        return _weights_cached(self._stages(x, sizes, w13, w2, dy), quantize_weights)
+
+    def _stages(self, x, sizes, w13, w2, dy):
         E, T, D, H, Tc, m = self.E, self.T, self.D, self.H, self.Tcap, self.mode
         mxw = self.wgrad == "mx"
         z0, z1 = self.z[:, :H], self.z[:, H:]

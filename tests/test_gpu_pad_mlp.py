@@ -136,3 +136,23 @@ def test_moe_mlp_step_matches_oracle(gpu, wgrad):
     for g in (0, 2, 3):
         assert _sqnr(rdw2[g], dw2[g]) > 35
         assert _sqnr(rdw13[g], dw13[g]) > 35
+
+
+def test_moe_step_with_cached_weight_quantization(gpu):
+    """Micro-batches of one optimizer step share one dual quantization of
+    the expert weights: a step that reuses the cached MXFP8 weights gives the
+    same bytes as a step that quantizes them again."""
+    E, T, D, H = 4, 600, 256, 128
+    sizes = to_dev(np.array([250, 0, 300, 50], np.int32))
+    Tcap = synth.capacity(T, E)
+    x, w1, w3, w2, dy = synth.mlp_inputs(T, D, H, E=E, seed=4)
+    x2, _, _, _, dy2 = synth.mlp_inputs(T, D, H, E=E, seed=5)
+    w13 = torch.cat([w1, w3], dim=1).to(dev())
+    w2 = w2.to(dev())
+    cached = mlp.MoEMLP(E, T, D, H, Tcap, dev())
+    cached.step(x.to(dev()), sizes, w13, w2, dy.to(dev()))
+    cached.step(x2.to(dev()), sizes, w13, w2, dy2.to(dev()), quantize_weights=False)
+    fresh = mlp.MoEMLP(E, T, D, H, Tcap, dev())
+    fresh.step(x2.to(dev()), sizes, w13, w2, dy2.to(dev()))
+    for k in ("y", "dx", "dw13", "dw2"):
+        assert torch.equal(getattr(cached, k), getattr(fresh, k)), k
