@@ -280,6 +280,16 @@ __device__ __forceinline__ void zero_tile(const TileSpec& ts) {
   const int esz = ts.out_f32 ? 4 : 2;
   const int row_bytes = ts.valid_n * esz;
   uint8_t* base = reinterpret_cast<uint8_t*>(ts.out);
+  const int64_t pitch = ts.ldo * esz;
+  if (ts.valid_n == kBN && ((reinterpret_cast<uintptr_t>(base) | (uintptr_t)pitch) & 15) == 0) {
+    // whole rows of 16-byte stores: 64 (fp32) or 32 (bf16) lanes per row
+    const int lanes_per_row = row_bytes >> 4;
+    const int rows_per_pass = kGemmThreads / lanes_per_row;
+    const int c = threadIdx.x % lanes_per_row;
+    for (int r = threadIdx.x / lanes_per_row; r < ts.valid_m; r += rows_per_pass)
+      reinterpret_cast<uint4*>(base + r * pitch)[c] = make_uint4(0, 0, 0, 0);
+    return;
+  }
   for (int r = threadIdx.x >> 4; r < ts.valid_m; r += kGemmThreads / 16) {
     uint8_t* row = base + (int64_t)r * ts.ldo * esz;
     for (int c = (threadIdx.x & 15) * 4; c < row_bytes; c += 64)
