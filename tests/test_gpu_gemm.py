@@ -264,3 +264,81 @@ def test_moe_grouped_shapes_sampled(gpu):
             ref = O.scaled_mm(*_oracle_rows(x_pad, rows), *_oracle_rows(w[e], cols))
             _check(got[rows][:, cols], None, None, ref, torch.bfloat16, f"group {e}")
         start = end
+
+
+
+def _moe_scout_groups():
+    E, T = 16, 16384
+    sizes = synth.zipf_group_sizes(T, E, 14)
+    Tcap = synth.capacity(T, E)
+    slots = -(-sizes // 128) * 128
+    return E, Tcap, _offsets(slots)
+
+
+def _oracle_cols(t_dev, cols):
+    """The oracle's quantization along dim 0 (tokens) of selected columns of
+    a device bf16 [Tcap, C] tensor: row-wise quantization of those rows of
+    its transpose (the column-wise layout's rows)."""
+    q = O.quantize_bf16(bf16_host(t_dev[:, cols].T.contiguous()), "rceil")
+    return q["q_row"], q["s_row"]
+
+
+def test_moe_wgrad_full_size_sampled(gpu):
+    """The MoE Scout w13 weight gradient in the benchmark's launch
+    configuration: dW [16, 16384, 5120] float32 from column-wise MXFP8
+    dZ [18432, 16384] and X [18432, 5120] over the Zipf groups (2 empty).
+    Empty groups' dW is exactly zero; 24 x 24 sampled entries of every other
+    group match the oracle, which quantizes the sampled rows of dZ^T and X^T
+    along the tokens itself and contracts over the group's tokens."""
+    E, Tcap, offs = _moe_scout_groups()
+    N, K = 16384, 5120
+    g = synth.generator(11, dev())
+    dz = synth.normal_bf16((Tcap, N), 1.0, g, dev())
+    x = synth.normal_bf16((Tcap, K), 1.0, g, dev())
+    qg = mx.quantize(dz, "rceil", rowwise=False, colwise=True)
+    qx = mx.quantize(x, "rceil", rowwise=False, colwise=True)
+    got = mx.grouped_mm_wgrad(qg["q_col"], qg["s_col"], qx["q_col"], qx["s_col"], to_dev(offs), torch.float32)
+    rng = np.random.default_rng(2)
+    rows = torch.as_tensor(np.sort(rng.choice(N, 24, replace=False)), device=dev())
+    cols = torch.as_tensor(np.sort(rng.choice(K, 24, replace=False)), device=dev())
+    qa, sa = _oracle_cols(dz, rows)
+    qb, sb = _oracle_cols(x, cols)
+    np.testing.assert_array_equal(host(qg["q_col"][rows]), qa)
+    start = 0
+    for e in range(E):
+        end = int(offs[e])
+        if end == start:
+            assert torch.all(got[e] == 0), f"empty group {e}"
+            continue
+        A = (qa[:, start:end], sa[:, start // 32:end // 32])
+        B = (qb[:, start:end], sb[:, start // 32:end // 32])
+        ref = O.scaled_mm(*A, *B)
+        _check(got[e][rows][:, cols], O.dequantize(*A), O.dequantize(*B), ref, torch.float32, f"group {e}")
+        start = end
+
+
+def test_moe_dgrad_full_size_sampled(gpu):
+    """The MoE Scout w13 input gradient: dX [18432, 5120] bf16 from row-wise
+    MXFP8 dZ [18432, 16384] and the experts' w13 quantized along 2H
+    ([16, 5120, 16384] column-wise), Zipf groups; the tail is zero and 16
+    sampled rows of every non-empty group x 96 sampled columns match the
+    oracle."""
+    E, Tcap, offs = _moe_scout_groups()
+    N, K = 5120, 16384                      # output columns (D), contraction (2H)
+    g = synth.generator(12, dev())
+    dz = synth.normal_bf16((Tcap, K), 1.0, g, dev())
+    w = synth.normal_bf16((E, K, N), 0.02, g, dev())     # w13 [E, 2H, D]
+    qd = mx.quantize(dz, "rceil")
+    qw = mx.quantize(w, "rceil", rowwise=False, colwise=True)  # [E, D, 2H]
+    got = mx.grouped_mm_dgrad(qd["q_row"], qd["s_row"], qw["q_col"], qw["s_col"], to_dev(offs), torch.bfloat16)
+    assert torch.all(got[int(offs[-1]):] == 0)
+    rng = np.random.default_rng(3)
+    cols = torch.as_tensor(np.sort(rng.choice(N, 96, replace=False)), device=dev())
+    start = 0
+    for e in range(E):
+        end = int(offs[e])
+        if end > start:
+            rows = torch.as_tensor(np.sort(rng.choice(np.arange(start, end), 16, replace=False)), device=dev())
+            ref = O.scaled_mm(*_oracle_rows(dz, rows), *_oracle_cols(w[e], cols))
+            _check(got[rows][:, cols], None, None, ref, torch.bfloat16, f"group {e}")
+        start = end

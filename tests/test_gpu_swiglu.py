@@ -93,3 +93,37 @@ def test_swiglu_special_values(gpu):
     for k in ("q_row", "s_row", "q_col", "s_col"):
         np.testing.assert_array_equal(host(got[k]) & (0x7F if k[0] == "q" else 0xFF),
                                       ref[k] & (0x7F if k[0] == "q" else 0xFF))
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_swiglu_full_size_sampled(gpu, direction):
+    """The MoE Scout SwiGLU boundary in the benchmark's launch configuration
+    (z = [a | b] of [18432, 16384], h of [18432, 8192]): 32 sampled rows
+    of the row-wise output and 32 sampled columns of the column-wise output
+    against the oracle, which evaluates only those rows / columns."""
+    T, H = 18432, 8192
+    g = synth.generator(21 if direction == "fwd" else 22, dev())
+    z = synth.normal_bf16((T, 2 * H), 2.0, g, dev())
+    a, b = z[:, :H], z[:, H:]
+    dh = synth.normal_bf16((T, H), 1.0, g, dev())
+    rng = np.random.default_rng(4)
+    # 32 of each: the oracle's dual quantization blocks both axes by 32
+    rows = torch.as_tensor(np.sort(rng.choice(T, 32, replace=False)), device=dev())
+    hcols = np.sort(rng.choice(H, 32, replace=False))
+    if direction == "fwd":
+        got = mx.swiglu_quant_fwd(a, b, "rceil")
+        ref_r = O.swiglu_quant_fwd(bf16_host(a[rows]), bf16_host(b[rows]), "rceil")
+        c = torch.as_tensor(hcols, device=dev())
+        ref_c = O.swiglu_quant_fwd(bf16_host(a[:, c]), bf16_host(b[:, c]), "rceil")
+        col_rows = hcols
+    else:
+        got = mx.swiglu_quant_bwd(dh, a, b, "rceil")
+        ref_r = O.swiglu_quant_bwd(bf16_host(dh[rows]), bf16_host(a[rows]), bf16_host(b[rows]), "rceil")
+        c = torch.as_tensor(hcols, device=dev())
+        ref_c = O.swiglu_quant_bwd(bf16_host(dh[:, c]), bf16_host(a[:, c]), bf16_host(b[:, c]), "rceil")
+        col_rows = np.concatenate([hcols, H + hcols])   # dA columns, then dB columns of [dA | dB]
+    _assert_close_codes((host(got["q_row"][rows]), plain(host(got["s_row"][:, rows]))),
+                        (ref_r["q_row"], ref_r["s_row"]), "row")
+    qc = host(got["q_col"][torch.as_tensor(col_rows, device=dev())])
+    sc = plain(host(got["s_col"][:, torch.as_tensor(col_rows, device=dev())]))
+    _assert_close_codes((qc, sc), (ref_c["q_col"], ref_c["s_col"]), "col")
