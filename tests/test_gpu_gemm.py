@@ -342,3 +342,69 @@ def test_moe_dgrad_full_size_sampled(gpu):
             ref = O.scaled_mm(*_oracle_rows(dz, rows), *_oracle_cols(w[e], cols))
             _check(got[rows][:, cols], None, None, ref, torch.bfloat16, f"group {e}")
         start = end
+
+
+def test_dsv3_full_size_sampled(gpu):
+    """The DeepSeek-V3-like expert share in the benchmark's launch
+    configuration (32 experts, 65536 routed token slots with Dirichlet(0.3)
+    group sizes padded to 128, D=7168, H=2048): the grouped w13 forward on
+    sampled rows of every non-empty group, and the w2 weight gradient both in
+    MXFP8 (float32 dW) and as wgrad_with_hp (bf16 operands, bf16 dW) on
+    sampled entries of every group. The oracle evaluates the same GEMMs on
+    the sampled rows / columns only."""
+    E, D, H, T = 32, 7168, 2048, 65536
+    sizes = synth.dirichlet_group_sizes(T, E, 0.3)
+    Tcap = synth.capacity(T, E)
+    offs = _offsets(-(-sizes // 128) * 128)
+    offs_d = to_dev(offs)
+    g = synth.generator(13, dev())
+    rng = np.random.default_rng(5)
+    # w13 forward: [Tcap, D] x [E, 2H, D]
+    x = synth.normal_bf16((Tcap, D), 1.0, g, dev())
+    w = synth.normal_bf16((E, 2 * H, D), 0.02, g, dev())
+    qx, qw = mx.quantize(x, "rceil"), mx.quantize(w, "rceil")
+    got = mx.grouped_mm_fwd(qx["q_row"], qx["s_row"], qw["q_row"], qw["s_row"], offs_d, torch.bfloat16)
+    assert torch.all(got[int(offs[-1]):] == 0)
+    cols = torch.as_tensor(np.sort(rng.choice(2 * H, 64, replace=False)), device=dev())
+    start = 0
+    for e in range(E):
+        end = int(offs[e])
+        if end > start:
+            rows = torch.as_tensor(np.sort(rng.choice(np.arange(start, end), 8, replace=False)), device=dev())
+            ref = O.scaled_mm(*_oracle_rows(x, rows), *_oracle_rows(w[e], cols))
+            _check(got[rows][:, cols], None, None, ref, torch.bfloat16, f"fwd group {e}")
+        start = end
+    del x, w, qx, qw, got
+    # w2 weight gradient: dW2[g] = dY_g^T h_g, [E, D, H]
+    dy = synth.normal_bf16((Tcap, D), 1.0, g, dev())
+    h = synth.normal_bf16((Tcap, H), 1.0, g, dev())
+    rows = torch.as_tensor(np.sort(rng.choice(D, 24, replace=False)), device=dev())
+    cols = torch.as_tensor(np.sort(rng.choice(H, 24, replace=False)), device=dev())
+    qd = mx.quantize(dy, "rceil", rowwise=False, colwise=True)
+    qh = mx.quantize(h, "rceil", rowwise=False, colwise=True)
+    got = mx.grouped_mm_wgrad(qd["q_col"], qd["s_col"], qh["q_col"], qh["s_col"], offs_d, torch.float32)
+    qa, sa = _oracle_cols(dy, rows)
+    qb, sb = _oracle_cols(h, cols)
+    ref = O.grouped_mm_wgrad(qa, sa, qb, sb, offs)
+    start = 0
+    for e in range(E):
+        end = int(offs[e])
+        if end == start:
+            assert torch.all(got[e] == 0), f"empty group {e}"
+        else:
+            A = O.dequantize(qa[:, start:end], sa[:, start // 32:end // 32])
+            B = O.dequantize(qb[:, start:end], sb[:, start // 32:end // 32])
+            _check(got[e][rows][:, cols], A, B, ref[e], torch.float32, f"wgrad group {e}")
+        start = end
+    del got, qd, qh
+    got = mx.grouped_mm_wgrad_hp(dy, h, offs_d)
+    ref = O.grouped_mm_wgrad_hp(bf16_host(dy[:, rows]), bf16_host(h[:, cols]), offs)
+    start = 0
+    for e in range(E):
+        end = int(offs[e])
+        if end == start:
+            assert torch.all(got[e] == 0), f"empty group {e} (hp)"
+        else:
+            worst, strict = bf16_ulp_check(bf16_host(got[e][rows][:, cols]), ref[e])
+            assert worst <= 2.0, f"hp wgrad group {e}: {worst} ulp"
+        start = end
