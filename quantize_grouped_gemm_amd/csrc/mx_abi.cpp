@@ -225,6 +225,10 @@ static mx_status grouped_2d3d(const char* fn, const uint8_t* qa, const uint8_t* 
   MX_REQUIRE(N > 0 && N % 16 == 0, MX_ERR_SHAPE, "%s: N must be a positive multiple of 16", fn);
   MX_REQUIRE(K > 0 && K % 128 == 0, MX_ERR_SHAPE, "%s: K must be a positive multiple of 128", fn);
   MX_REQUIRE(Tcap / 256 + E <= 65535 && (N + 255) / 256 <= 65535, MX_ERR_SHAPE, "%s: too large", fn);
+  // the launch covers every possible row tile times the column tiles (plus
+  // the slack of the XCD deal) in one 1-D grid of int-indexed workgroups
+  MX_REQUIRE((Tcap / 256 + (E + 2) / 2 + 1) * ((N + 255) / 256) + 4096 <= 0x7FFFFFFF, MX_ERR_SHAPE,
+             "%s: too many tiles for one launch", fn);
   MX_REQUIRE(scales_fit(Tcap, K) && scales_fit(N, K), MX_ERR_SHAPE, "%s: scale matrices too large", fn);
   if (Tcap == 0) return MX_OK;
   MX_CHECK(check_mx_operand(fn, "A", qa, sa));

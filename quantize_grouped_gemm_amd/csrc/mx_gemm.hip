@@ -740,6 +740,27 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   return xcd * per + min(xcd, rem) + j;
 }
 
+// Deals tiles [0, total) to the 8 XCDs in chunks of kXcdChunk consecutive
+// tiles, round-robin: chunk k is XCD (k % 8)'s (k / 8)-th chunk. Workgroup b
+// (dispatched to XCD b % 8 as that XCD's (b >> 3)-th) gets its XCD's
+// (b >> 3)-th tile, or -1 past the end. Used where tile costs vary across
+// the tile order (grouped GEMMs: a band holding several small groups loads
+// more distinct B tiles), so that no XCD's share is all slow tiles. A chunk
+// is one round of the XCD's 32 CUs, so tiles running together still share
+// their band's A and B tiles in that XCD's L2.
+constexpr int kXcdChunk = 32;
+
+__device__ __forceinline__ int xcd_chunked(int b, int total) {
+  const int x = b & 7, j = b >> 3;
+  const int t = ((j / kXcdChunk) * 8 + x) * kXcdChunk + j % kXcdChunk;
+  return t < total ? t : -1;
+}
+
+// Workgroup indices the chunked deal of `total` tiles spans.
+__host__ __device__ constexpr int64_t xcd_chunked_span(int64_t total) {
+  return (total + 8 * kXcdChunk - 1) / (8 * kXcdChunk) * (8 * kXcdChunk);
+}
+
 // Tile index -> (row tile, column tile) in bands of kBandM row tiles, column
 // tiles walked within a band. `first` and `rows` return the band.
 __device__ __forceinline__ void band_order(int t, int mt, int nt, int& m, int& n, int& first, int& rows) {
@@ -874,14 +895,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   const int mt_groups = tile_end[a.E - 1]; // row tiles of the groups
   const int nt = (int)((a.N + kBN - 1) / kBN);
   const int b = (int)blockIdx.x;
-  if (b >= mt * nt) return;
-  // the groups' tiles are dealt to the XCDs in equal contiguous runs; the
-  // tail's zero tiles come after them, so no XCD's run is padded with them
+  // the groups' tiles are dealt to the XCDs in chunks; the tail's zero tiles
+  // follow the span of that deal, so no XCD's share is padded with them
+  const int span = (int)xcd_chunked_span((int64_t)mt_groups * nt);
   int tile, tn, bfirst, brows;
-  if (b < mt_groups * nt) {
-    band_order(xcd_remap(b, mt_groups * nt), mt_groups, nt, tile, tn, bfirst, brows);
+  if (b < span) {
+    const int t = xcd_chunked(b, mt_groups * nt);
+    if (t < 0) return;
+    band_order(t, mt_groups, nt, tile, tn, bfirst, brows);
   } else {
-    const int z = b - mt_groups * nt;
+    const int z = b - span;
+    if (z >= (mt - mt_groups) * nt) return;
     tile = mt_groups + z / nt;
     tn = z % nt;
     bfirst = tile;
@@ -1006,7 +1030,9 @@ hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) {
   // sum over E groups + tail of ceil(rows / 256) with rows multiples of 128
   const int64_t mtiles = a.M / kBM + (a.E + 2) / 2 + 1;
-  const int64_t tiles = mtiles * ((a.N + kBN - 1) / kBN);
+  // the chunked deal of the groups' tiles spans at most 8 * kXcdChunk - 1
+  // indices more than the tiles themselves
+  const int64_t tiles = mtiles * ((a.N + kBN - 1) / kBN) + 8 * kXcdChunk;
   hipLaunchKernelGGL(k_gemm_grouped, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a);
   return hipGetLastError();
 }
