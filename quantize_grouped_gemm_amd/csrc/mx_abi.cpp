@@ -199,6 +199,8 @@ mx_status mx_scaled_mm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
   MX_REQUIRE(out_dtype == MX_BF16 || out_dtype == MX_F32, MX_ERR_ARG, "%s: bad dtype", fn);
   MX_REQUIRE(M >= 0 && N >= 0 && K > 0 && K % 128 == 0, MX_ERR_SHAPE, "%s: K (%lld) must be a positive multiple of 128", fn, (long long)K);
   MX_REQUIRE((M + 255) / 256 <= 65535 && (N + 255) / 256 <= 65535, MX_ERR_SHAPE, "%s: M or N too large", fn);
+  MX_REQUIRE((M + 255) / 256 * ((N + 255) / 256) + 4096 <= 0x7FFFFFFF, MX_ERR_SHAPE,
+             "%s: too many tiles for one launch", fn);
   MX_REQUIRE(scales_fit(M, K) && scales_fit(N, K), MX_ERR_SHAPE, "%s: scale matrices too large", fn);
   if (M == 0 || N == 0) return MX_OK;
   MX_CHECK(check_mx_operand(fn, "A", qa, sa));

@@ -30,9 +30,12 @@
 // of 16, so the pass is free of bank conflicts (and so are 8-lane groups).
 //
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs, each
-// with its own L2. The linear workgroup index is remapped so that each XCD
-// takes a contiguous run of tiles, and tiles are numbered in bands of 8 row
-// tiles, so the ~32 workgroups resident on one XCD share A and B tiles.
+// with its own L2. Tiles are numbered in bands of 8 row tiles (column tiles
+// walked within a band), and the dense and grouped kernels deal chunks of 32
+// consecutive tiles to the XCDs round-robin, so the 32 workgroups resident
+// on one XCD share A and B tiles while every XCD gets a spread of the tile
+// order. The weight-gradient kernel gives each XCD an equal contiguous share
+// of every group instead (its groups run one after another).
 //
 // MFMA operand layout (32x32x64, 8-bit elements, measured on the device):
 // lane l holds row (l & 31) of its 32-row block; with h = l >> 5 its bytes
@@ -834,7 +837,9 @@ __device__ __forceinline__ int64_t group_start(const int32_t* ends, int g) {
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dense(GemmArgs a) {
   const int mt = (int)((a.M + kBM - 1) / kBM), nt = (int)((a.N + kBN - 1) / kBN);
   int tm, tn, bfirst, brows;
-  band_order(xcd_remap(blockIdx.x, mt * nt), mt, nt, tm, tn, bfirst, brows);
+  const int t = xcd_chunked(blockIdx.x, mt * nt);
+  if (t < 0) return;
+  band_order(t, mt, nt, tm, tn, bfirst, brows);
   const int64_t m0 = (int64_t)tm * kBM;
   const int64_t n0 = (int64_t)tn * kBN;
   TileSpec ts;
@@ -1022,7 +1027,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_wgrad(GemmArgs a) {
 
 
 hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s) {
-  const int64_t tiles = ((a.N + kBN - 1) / kBN) * ((a.M + kBM - 1) / kBM);
+  const int64_t tiles = xcd_chunked_span(((a.N + kBN - 1) / kBN) * ((a.M + kBM - 1) / kBM));
   hipLaunchKernelGGL(k_gemm_dense, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a);
   return hipGetLastError();
 }
