@@ -208,6 +208,35 @@ mx_status mx_scaled_grouped_mm_dgrad(const uint8_t* qa, const uint8_t* sa,
                                      mx_dtype out_dtype, void* out,
                                      int32_t* dev_err, void* stream);
 
+/* The grouped forward and input gradient with the result in token order:
+ * the per-group padding is undone by the GEMM itself (the padded expert-major
+ * layout exists only for the kernels, [P3], The integration). Arguments as
+ * for mx_scaled_grouped_mm_fwd / _dgrad, plus group_sizes: device int32 [E],
+ * the tokens of each group (the sizes given to mx_pad_groups /
+ * mx_pad_quantize), and T, the routed tokens. out [T, N]: group g's first
+ * group_sizes[g] rows of its padded slot go, in order, to out rows
+ * [sum(group_sizes[0:g]), + group_sizes[g]). Pad rows and the tail are
+ * computed nowhere and written nowhere. The same as unpadding the padded
+ * result (mx_unpad_groups) bit for bit. A size that is negative or exceeds
+ * its group's padded slot, or sizes summing past T, set bit 2 of *dev_err;
+ * rows that would fall outside the slot or out are then dropped. */
+mx_status mx_scaled_grouped_mm_fwd_unpad(const uint8_t* qa, const uint8_t* sa,
+                                         const uint8_t* qw, const uint8_t* sw,
+                                         const int32_t* offs,
+                                         const int32_t* group_sizes, int32_t E,
+                                         int64_t Tcap, int64_t T, int64_t N,
+                                         int64_t K, mx_dtype out_dtype,
+                                         void* out, int32_t* dev_err,
+                                         void* stream);
+mx_status mx_scaled_grouped_mm_dgrad_unpad(const uint8_t* qa, const uint8_t* sa,
+                                           const uint8_t* qw, const uint8_t* sw,
+                                           const int32_t* offs,
+                                           const int32_t* group_sizes,
+                                           int32_t E, int64_t Tcap, int64_t T,
+                                           int64_t N, int64_t K,
+                                           mx_dtype out_dtype, void* out,
+                                           int32_t* dev_err, void* stream);
+
 /* MXFP8 grouped GEMM, weight gradient, 2-D x 2-D: the contraction runs over
  * each group's own tokens. dW[g] = deq(G^T)[:, s_g:e_g] * deq(X^T)[:, s_g:e_g]^T
  * qg [N, Tcap], sg: dY column-wise (quantized along tokens).

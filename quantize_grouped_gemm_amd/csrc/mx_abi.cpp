@@ -220,7 +220,8 @@ mx_status mx_scaled_mm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
 
 static mx_status grouped_2d3d(const char* fn, const uint8_t* qa, const uint8_t* sa, const uint8_t* qw,
                               const uint8_t* sw, const int32_t* offs, int32_t E, int64_t Tcap, int64_t N,
-                              int64_t K, mx_dtype out_dtype, void* out, int32_t* dev_err, void* stream) {
+                              int64_t K, mx_dtype out_dtype, void* out, int32_t* dev_err, void* stream,
+                              const int32_t* sizes = nullptr, int64_t T = 0) {
   MX_REQUIRE(out_dtype == MX_BF16 || out_dtype == MX_F32, MX_ERR_ARG, "%s: bad dtype", fn);
   MX_REQUIRE(E >= 1 && E <= 1024, MX_ERR_SHAPE, "%s: E (%d) must be in [1, 1024]", fn, E);
   MX_REQUIRE(Tcap >= 0 && Tcap % 128 == 0, MX_ERR_SHAPE, "%s: Tcap must be a multiple of 128", fn);
@@ -245,7 +246,36 @@ static mx_status grouped_2d3d(const char* fn, const uint8_t* qa, const uint8_t* 
   a.b_group_stride = N * K; a.sb_group_stride = N * (K / 32);
   a.out = out; a.ldo = N; a.out_f32 = out_dtype == MX_F32;
   a.offs = offs; a.E = E; a.dev_err = dev_err;
+  a.sizes = sizes; a.out_rows = T;
   return launched(mxk::launch_gemm_grouped(a, as_stream(stream)), fn);
+}
+
+// Token-order variants: the output holds the T routed tokens, not the
+// padded rows.
+static mx_status grouped_2d3d_unpad(const char* fn, const uint8_t* qa, const uint8_t* sa, const uint8_t* qw,
+                                    const uint8_t* sw, const int32_t* offs, const int32_t* group_sizes,
+                                    int32_t E, int64_t Tcap, int64_t T, int64_t N, int64_t K, mx_dtype out_dtype,
+                                    void* out, int32_t* dev_err, void* stream) {
+  MX_REQUIRE(T >= 0 && T <= Tcap, MX_ERR_SHAPE, "%s: T (%lld) must be in [0, Tcap]", fn, (long long)T);
+  MX_REQUIRE(Tcap == 0 || group_sizes, MX_ERR_NULL, "%s: group_sizes NULL", fn);
+  if (T == 0) return MX_OK;
+  return grouped_2d3d(fn, qa, sa, qw, sw, offs, E, Tcap, N, K, out_dtype, out, dev_err, stream, group_sizes, T);
+}
+
+mx_status mx_scaled_grouped_mm_fwd_unpad(const uint8_t* qa, const uint8_t* sa, const uint8_t* qw,
+                                         const uint8_t* sw, const int32_t* offs, const int32_t* group_sizes,
+                                         int32_t E, int64_t Tcap, int64_t T, int64_t N, int64_t K,
+                                         mx_dtype out_dtype, void* out, int32_t* dev_err, void* stream) {
+  return grouped_2d3d_unpad("mx_scaled_grouped_mm_fwd_unpad", qa, sa, qw, sw, offs, group_sizes, E, Tcap, T, N,
+                            K, out_dtype, out, dev_err, stream);
+}
+
+mx_status mx_scaled_grouped_mm_dgrad_unpad(const uint8_t* qa, const uint8_t* sa, const uint8_t* qw,
+                                           const uint8_t* sw, const int32_t* offs, const int32_t* group_sizes,
+                                           int32_t E, int64_t Tcap, int64_t T, int64_t N, int64_t K,
+                                           mx_dtype out_dtype, void* out, int32_t* dev_err, void* stream) {
+  return grouped_2d3d_unpad("mx_scaled_grouped_mm_dgrad_unpad", qa, sa, qw, sw, offs, group_sizes, E, Tcap, T,
+                            N, K, out_dtype, out, dev_err, stream);
 }
 
 mx_status mx_scaled_grouped_mm_fwd(const uint8_t* qa, const uint8_t* sa, const uint8_t* qw, const uint8_t* sw,

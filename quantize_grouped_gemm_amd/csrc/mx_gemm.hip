@@ -873,8 +873,37 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dense(GemmArgs a) {
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   __shared__ int32_t ends[kMaxGroups + 1];
   __shared__ int32_t tile_end[kMaxGroups + 1];   // inclusive prefix of row-tile counts
+  __shared__ int32_t tok[kMaxGroups + 1];        // token-order output: first row of each group
   const bool reporter = blockIdx.x == 0;
   load_group_ends(a.offs, a.E, a.M, ends, a.dev_err, reporter);
+  if (a.sizes && threadIdx.x < 64) {
+    // exclusive prefix of the token counts; a count beyond its group's
+    // padded slot, or a total beyond out_rows, is reported (bit 2)
+    const int lane = threadIdx.x;
+    int32_t carry = 0;
+    bool bad = false;
+    for (int g0 = 0; g0 < a.E; g0 += 64) {
+      const int g = g0 + lane;
+      int32_t n = g < a.E ? a.sizes[g] : 0;
+      if (g < a.E) {
+        const int32_t slot = ends[g] - (int32_t)group_start(ends, g);
+        bad |= n < 0 || n > slot;
+        n = min(max(n, 0), slot);
+      }
+      int32_t v = n;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int32_t o = __shfl_up(v, d);
+        if (lane >= d) v += o;
+      }
+      if (g < a.E) tok[g] = carry + v - n;
+      carry += __shfl(v, 63);
+    }
+    bad |= (int64_t)carry > a.out_rows;
+    const bool any_bad = __any(bad);   // every lane votes
+    if (lane == 0) tok[a.E] = carry;
+    if (reporter && lane == 0 && any_bad && a.dev_err) atomicOr(a.dev_err, 4);
+  }
   if (threadIdx.x < 64) {
     // row-tile counts of groups 0..E (E = the tail), inclusive prefix sum
     const int lane = threadIdx.x;
@@ -944,13 +973,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   ts.valid_n = (int)min<int64_t>(kBN, a.N - n0);
   ts.k_begin = 0;
   ts.nk = g < a.E ? (int)(a.K / kBK) : 0;
+  int64_t out_row = m0;
+  if (a.sizes) {
+    // token order: only the group's real rows, shifted to its token range
+    if (g >= a.E) return;                              // no tail rows
+    const int64_t in_group = m0 - gs;
+    const int64_t real = (int64_t)(tok[g + 1] - tok[g]) - in_group;
+    out_row = tok[g] + in_group;
+    const int64_t room = a.out_rows - out_row;
+    const int64_t rows = min<int64_t>(min<int64_t>(real, room), ts.valid_m);
+    if (rows <= 0) return;
+    ts.valid_m = (int)rows;
+  }
   {
     // the band's row tiles that belong to group g share its B tiles
     const int lo = max(bfirst, first), hi = min(bfirst + brows, tile_end[g]);
     set_prefetch_shares(ts, tn, tile - lo, hi - lo);
   }
   const int esz = a.out_f32 ? 4 : 2;
-  ts.out = reinterpret_cast<uint8_t*>(a.out) + (m0 * a.ldo + n0) * esz;
+  ts.out = reinterpret_cast<uint8_t*>(a.out) + (out_row * a.ldo + n0) * esz;
   ts.ldo = a.ldo;
   ts.out_f32 = a.out_f32;
   gemm_tile(ts);

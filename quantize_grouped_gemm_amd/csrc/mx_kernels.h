@@ -60,6 +60,11 @@ struct GemmArgs {
   const int32_t* offs;
   int32_t E;
   int32_t* dev_err;
+  // grouped fwd/dgrad with the output in token order (optional): group g's
+  // first sizes[g] rows go to out rows [sum(sizes[0:g]), + sizes[g]); pad
+  // rows and the tail are not written. out has out_rows rows.
+  const int32_t* sizes = nullptr;
+  int64_t out_rows = 0;
 };
 
 struct PadArgs {

@@ -18,8 +18,9 @@ quoted on the TrainingWeightWrapperTensor page):
             dZ   = SwiGLU backward            (fused kernel, dual quantized)
             dx   = dZ w13                     (w13 quantized along 2H)
             dW13 = dZ^T x
-The grouped variant pads each expert's tokens to a multiple of 128 first,
-runs the grouped GEMMs over the padded offsets and unpads y and dx. With the
+The grouped variant pads each expert's tokens to a multiple of 128 first
+and runs the grouped GEMMs over the padded offsets; the w2 forward and the
+w13 input gradient write y and dx straight in token order. With the
 MXFP8 weight gradient the padding of x and dy is fused into their
 quantization (no bf16 padded copy); the hp recipe keeps the bf16 copies,
 which its weight-gradient GEMM reads.
@@ -179,13 +180,11 @@ class MoEMLP:
         self.hq = _q_out((), Tcap, H, dev)
         if not mxw:
             self.hq["h"] = torch.empty((Tcap, H), dtype=bf, device=dev)
-        self.y_pad = torch.empty((Tcap, D), dtype=bf, device=dev)
         self.y = torch.empty((T, D), dtype=bf, device=dev)
         self.dh = torch.empty((Tcap, H), dtype=bf, device=dev)
         self.dzq = _q_out((), Tcap, 2 * H, dev)
         if not mxw:
             self.dzq["dab"] = torch.empty((Tcap, 2 * H), dtype=bf, device=dev)
-        self.dx_pad = torch.empty((Tcap, D), dtype=bf, device=dev)
         self.dx = torch.empty((T, D), dtype=bf, device=dev)
         wdt = wgrad_dtype if mxw else bf
         self.dw2 = torch.empty((E, D, H), dtype=wdt, device=dev)
@@ -233,11 +232,10 @@ class MoEMLP:
                                             self.q13["s_row"], self.offs, out=self.z, dev_err=err)),
             Stage("swiglu_fwd", "k_swiglu_fwd", 0, Tc * H * (4 + 2 * (1 + 1 / 32) + (0 if mxw else 2)),
                   lambda: mx.swiglu_quant_fwd(z0, z1, m, want_h=not mxw, out=self.hq)),
+            # y straight in token order: the GEMM drops the pad rows itself
             Stage("gemm_w2_fwd", "k_gemm_grouped", 2 * T * D * H, 0,
-                  lambda: mx.grouped_mm_fwd(self.hq["q_row"], self.hq["s_row"], self.q2["q_row"],
-                                            self.q2["s_row"], self.offs, out=self.y_pad, dev_err=err)),
-            Stage("unpad_y", "k_unpad", 0, 4 * T * D,
-                  lambda: mx.unpad_groups(self.y_pad, self.src, T, out=self.y)),
+                  lambda: mx.grouped_mm_fwd_unpad(self.hq["q_row"], self.hq["s_row"], self.q2["q_row"],
+                                                  self.q2["s_row"], self.offs, sizes, T, out=self.y, dev_err=err)),
         ]
         if mxw:
             st.append(Stage("pad_quant_dy", "k_quant_tile", 0, _pad_qbytes(T, Tc, D),
@@ -269,10 +267,9 @@ class MoEMLP:
             Stage("swiglu_bwd", "k_swiglu_bwd", 0, Tc * H * (6 + 4 * (1 + 1 / 32) + (0 if mxw else 4)),
                   lambda: mx.swiglu_quant_bwd(self.dh, z0, z1, m, want_dab=not mxw, out=self.dzq)),
             Stage("gemm_w13_dgrad", "k_gemm_grouped", 2 * T * 2 * H * D, 0,
-                  lambda: mx.grouped_mm_dgrad(self.dzq["q_row"], self.dzq["s_row"], self.q13["q_col"],
-                                              self.q13["s_col"], self.offs, out=self.dx_pad, dev_err=err)),
-            Stage("unpad_dx", "k_unpad", 0, 4 * T * D,
-                  lambda: mx.unpad_groups(self.dx_pad, self.src, T, out=self.dx)),
+                  lambda: mx.grouped_mm_dgrad_unpad(self.dzq["q_row"], self.dzq["s_row"], self.q13["q_col"],
+                                                    self.q13["s_col"], self.offs, sizes, T, out=self.dx,
+                                                    dev_err=err)),
         ]
         if mxw:
             st.append(Stage("gemm_w13_wgrad", "k_gemm_wgrad", 2 * T * 2 * H * D, 0,

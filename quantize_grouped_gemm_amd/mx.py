@@ -44,6 +44,10 @@ _SIGS = {
                                  ctypes.c_int),
     "mx_scaled_grouped_mm_dgrad": ([_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P],
                                    ctypes.c_int),
+    "mx_scaled_grouped_mm_fwd_unpad": ([_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, ctypes.c_int, _P,
+                                        _P, _P], ctypes.c_int),
+    "mx_scaled_grouped_mm_dgrad_unpad": ([_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, ctypes.c_int, _P,
+                                          _P, _P], ctypes.c_int),
     "mx_scaled_grouped_mm_wgrad": ([_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P],
                                    ctypes.c_int),
     "mx_grouped_mm_wgrad_hp": ([_P, _P, _P, _I32, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
@@ -208,6 +212,30 @@ def grouped_mm_fwd(qa, sa, qw, sw, offs, out_dtype=torch.bfloat16, out=None, dev
 
 def grouped_mm_dgrad(qa, sa, qw, sw, offs, out_dtype=torch.bfloat16, out=None, dev_err=None):
     return _grouped("mx_scaled_grouped_mm_dgrad", qa, sa, qw, sw, offs, out_dtype, out, dev_err)
+
+
+def _grouped_unpad(name, qa, sa, qw, sw, offs, sizes, T, out_dtype, out, dev_err):
+    Tcap, K = qa.shape
+    E, N = qw.shape[0], qw.shape[1]
+    if out is None:
+        out = torch.empty((T, N), dtype=out_dtype, device=qa.device)
+    st = getattr(lib(), name)(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _ptr(offs), _ptr(sizes), E, Tcap, T, N, K,
+                              _DT[out.dtype], _ptr(out), _ptr(dev_err), _stream(qa.device))
+    _check(st, name)
+    return out
+
+
+def grouped_mm_fwd_unpad(qa, sa, qw, sw, offs, sizes, T, out_dtype=torch.bfloat16, out=None, dev_err=None):
+    """grouped_mm_fwd with the result in token order [T, N] (sizes: int32
+    [E] tokens per group on the device)."""
+    return _grouped_unpad("mx_scaled_grouped_mm_fwd_unpad", qa, sa, qw, sw, offs, sizes, T, out_dtype, out,
+                          dev_err)
+
+
+def grouped_mm_dgrad_unpad(qa, sa, qw, sw, offs, sizes, T, out_dtype=torch.bfloat16, out=None, dev_err=None):
+    """grouped_mm_dgrad with the result in token order [T, N]."""
+    return _grouped_unpad("mx_scaled_grouped_mm_dgrad_unpad", qa, sa, qw, sw, offs, sizes, T, out_dtype, out,
+                          dev_err)
 
 
 def grouped_mm_wgrad(qg, sg, qx, sx, offs, out_dtype=torch.float32, out=None, dev_err=None):

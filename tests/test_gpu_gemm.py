@@ -140,6 +140,38 @@ def test_grouped_fwd_and_dgrad(gpu, out_dtype):
             start = end
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("sizes", [[250, 0, 300, 50], [128, 256, 1], [0, 0, 5], [700, 0, 0, 300, 129]])
+def test_grouped_token_order_equals_unpadded(gpu, sizes, out_dtype):
+    """The token-order fwd / dgrad write exactly the bytes that unpadding the
+    padded result gives (all rows of the output), and nothing for pad rows."""
+    sizes = np.array(sizes, np.int32)
+    E, T = len(sizes), int(sizes.sum())
+    Tcap = synth.capacity(T, E)
+    offs = _offsets(-(-sizes // 128) * 128)
+    N, K = 320, 256
+    src = O.pad_groups(np.zeros((T, 1), np.uint16), sizes, 128, Tcap)[2]
+    qa, sa, _ = real_mx((Tcap, K), 1.0, 7)
+    qw, sw, _ = real_mx((E, N, K), 0.05, 8)
+    args = (*_mx_dev(qa, sa), *_mx_dev(qw, sw), to_dev(offs))
+    for fn, fn_unpad in ((mx.grouped_mm_fwd, mx.grouped_mm_fwd_unpad),
+                         (mx.grouped_mm_dgrad, mx.grouped_mm_dgrad_unpad)):
+        padded = fn(*args, out_dtype)
+        ref = mx.unpad_groups(padded, to_dev(src), T)
+        err = torch.zeros(1, dtype=torch.int32, device=dev())
+        out = torch.full((T, N), float("nan"), dtype=out_dtype, device=dev())
+        got = fn_unpad(*args, to_dev(sizes), T, out_dtype, out=out, dev_err=err)
+        assert torch.equal(got, ref), fn.__name__
+        assert int(err.item()) == 0
+    # sizes that exceed their padded slot are reported
+    bad = sizes.copy()
+    bad[np.argmax(bad)] += 128
+    err = torch.zeros(1, dtype=torch.int32, device=dev())
+    mx.grouped_mm_fwd_unpad(*args, to_dev(bad), T, out_dtype, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 4
+
+
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_grouped_wgrad(gpu, out_dtype):
     E, N, K = 4, 272, 320
