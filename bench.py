@@ -228,6 +228,45 @@ def _linear_component(torch, dev, reps=50):
     return {"us_per_linear_fwd": round(a.elapsed_time(b) / reps * 1e3, 2), "shape": "256x256x512, bf16 out"}
 
 
+def _fused_swiglu_component(torch, dev, reps=5):
+    """The MoE Scout w13 forward with SwiGLU + dual quantization fused into
+    its epilogue, against the grouped forward followed by the standalone
+    fused SwiGLU kernel (what the step runs)."""
+    import numpy as np
+    from quantize_grouped_gemm_amd import mx, synth
+    c = synth.MOE_SCOUT
+    E, T, D, H = c["E"], c["T"], c["D"], c["H"]
+    sizes = synth.zipf_group_sizes(T, E, 14)
+    Tcap = synth.capacity(T, E)
+    offs = torch.tensor(np.cumsum(-(-sizes // 128) * 128).astype(np.int32), device=dev)
+    g = synth.generator(0, dev)
+    x = synth.normal_bf16((Tcap, D), 1.0, g, dev)
+    w = synth.normal_bf16((E, 2 * H, D), 0.02, g, dev)
+    qx, qw = mx.quantize(x, "rceil"), mx.quantize(w, "rceil")
+    del x, w
+    fo = mx.grouped_mm_swiglu_fwd(qx["q_row"], qx["s_row"], qw["q_row"], qw["s_row"], offs)
+    z = fo["z"]
+    so = mx.swiglu_quant_fwd(z[:, :H], z[:, H:], "rceil")
+
+    def timed(f):
+        f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3
+
+    fused = timed(lambda: mx.grouped_mm_swiglu_fwd(qx["q_row"], qx["s_row"], qw["q_row"], qw["s_row"], offs,
+                                                   out=fo))
+    gemm = timed(lambda: mx.grouped_mm_fwd(qx["q_row"], qx["s_row"], qw["q_row"], qw["s_row"], offs, out=z))
+    swi = timed(lambda: mx.swiglu_quant_fwd(z[:, :H], z[:, H:], "rceil", out=so))
+    return {"fused_us": round(fused, 1), "unfused_gemm_us": round(gemm, 1), "unfused_swiglu_us": round(swi, 1),
+            "unfused_total_us": round(gemm + swi, 1)}
+
+
 def _cpu_baseline():
     """The oracle on a bounded slice of the default workload: one expert with
     1024 of its 8192 hidden units and 128 tokens. Weight quantization and the
@@ -325,6 +364,8 @@ def main():
     if not args.no_components:
         comp = {"quantize_stress_32768x7168": _quant_component(torch, dev),
                 "linear_256x256x512": _linear_component(torch, dev)}
+        if name == "moe_scout":
+            comp["moe_scout_w13_fwd_fused_swiglu"] = _fused_swiglu_component(torch, dev)
         if name.startswith("moe"):
             # an optimizer step of 4 micro-batches: the expert weights are
             # dual-quantized once and their MXFP8 copies reused

@@ -208,6 +208,28 @@ mx_status mx_scaled_grouped_mm_dgrad(const uint8_t* qa, const uint8_t* sa,
                                      mx_dtype out_dtype, void* out,
                                      int32_t* dev_err, void* stream);
 
+/* The w13 grouped forward fused with the SwiGLU + dual MX quantization that
+ * follows it ([P3], The integration: fully fused grouped MLPs are the next
+ * MXFP8 fusion path): one launch computes z = deq(A) deq(W13_g)^T exactly as
+ * mx_scaled_grouped_mm_fwd does (W13 [E, 2H, K] = [w1; w3] per expert, gate
+ * rows first) and writes it to z (bf16 [Tcap, 2H], kept for the backward),
+ * and from the same tiles h = silu(z[:, :H]) * z[:, H:] quantized as
+ * mx_swiglu_quant_fwd would quantize it from z: q_row [Tcap, H] with s_row
+ * [H/128, Tcap, 4], q_col [H, Tcap] with s_col [Tcap/128, H, 4] (K128
+ * scales), the same bytes. h_out (bf16 [Tcap, H]) is optional. Rows past
+ * offs[E-1] give z = 0 and h = 0. H % 128 == 0, K % 128 == 0,
+ * Tcap % 128 == 0. */
+mx_status mx_scaled_grouped_mm_swiglu_fwd(const uint8_t* qa, const uint8_t* sa,
+                                          const uint8_t* qw13,
+                                          const uint8_t* sw13,
+                                          const int32_t* offs, int32_t E,
+                                          int64_t Tcap, int64_t H, int64_t K,
+                                          mx_scale_mode mode, void* z,
+                                          uint8_t* q_row, uint8_t* s_row,
+                                          uint8_t* q_col, uint8_t* s_col,
+                                          void* h_out, int32_t* dev_err,
+                                          void* stream);
+
 /* The grouped forward and input gradient with the result in token order:
  * the per-group padding is undone by the GEMM itself (the padded expert-major
  * layout exists only for the kernels, [P3], The integration). Arguments as

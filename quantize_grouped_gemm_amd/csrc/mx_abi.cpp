@@ -250,6 +250,41 @@ static mx_status grouped_2d3d(const char* fn, const uint8_t* qa, const uint8_t* 
   return launched(mxk::launch_gemm_grouped(a, as_stream(stream)), fn);
 }
 
+mx_status mx_scaled_grouped_mm_swiglu_fwd(const uint8_t* qa, const uint8_t* sa, const uint8_t* qw,
+                                          const uint8_t* sw, const int32_t* offs, int32_t E, int64_t Tcap,
+                                          int64_t H, int64_t K, mx_scale_mode mode, void* z, uint8_t* q_row,
+                                          uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, void* h_out,
+                                          int32_t* dev_err, void* stream) {
+  const char* fn = "mx_scaled_grouped_mm_swiglu_fwd";
+  MX_REQUIRE(mode == MX_RCEIL || mode == MX_FLOOR, MX_ERR_ARG, "%s: bad scale mode %d", fn, (int)mode);
+  MX_REQUIRE(E >= 1 && E <= 1024, MX_ERR_SHAPE, "%s: E (%d) must be in [1, 1024]", fn, E);
+  MX_REQUIRE(Tcap >= 0 && Tcap % 128 == 0, MX_ERR_SHAPE, "%s: Tcap must be a multiple of 128", fn);
+  MX_REQUIRE(H > 0 && H % 128 == 0, MX_ERR_SHAPE, "%s: H must be a positive multiple of 128", fn);
+  MX_REQUIRE(K > 0 && K % 128 == 0, MX_ERR_SHAPE, "%s: K must be a positive multiple of 128", fn);
+  MX_REQUIRE(Tcap / 256 + E <= 65535 && H / 128 <= 65535, MX_ERR_SHAPE, "%s: too large", fn);
+  MX_REQUIRE((Tcap / 256 + (E + 2) / 2 + 1) * (H / 128) + 4096 <= 0x7FFFFFFF, MX_ERR_SHAPE,
+             "%s: too many tiles for one launch", fn);
+  MX_REQUIRE(scales_fit(Tcap, K) && scales_fit(2 * H, K), MX_ERR_SHAPE, "%s: scale matrices too large", fn);
+  MX_REQUIRE(Tcap * 2 * H * 2 < (1ll << 40), MX_ERR_SHAPE, "%s: z too large", fn);
+  if (Tcap == 0) return MX_OK;
+  MX_CHECK(check_mx_operand(fn, "A", qa, sa));
+  MX_CHECK(check_mx_operand(fn, "W13", qw, sw));
+  MX_REQUIRE(offs && z && q_row && s_row && q_col && s_col, MX_ERR_NULL, "%s: NULL pointer", fn);
+  MX_REQUIRE(al16(z) && al16(q_row) && al16(q_col) && al4(s_row) && al4(s_col) && (!h_out || al16(h_out)),
+             MX_ERR_ALIGN, "%s: z/q/h must be 16-byte and scales 4-byte aligned", fn);
+  MX_DEVICE();
+  mxk::GemmArgs a{};
+  a.qa = qa; a.sa = sa; a.qb = qw; a.sb = sw;
+  a.M = Tcap; a.N = 2 * H; a.K = K;
+  a.lda = K; a.ldb = K; a.srows_a = Tcap; a.srows_b = 2 * H;
+  a.b_group_stride = 2 * H * K; a.sb_group_stride = 2 * H * (K / 32);
+  a.out = z; a.ldo = 2 * H; a.out_f32 = false;
+  a.offs = offs; a.E = E; a.dev_err = dev_err;
+  a.hq_row = q_row; a.hs_row = s_row; a.hq_col = q_col; a.hs_col = s_col;
+  a.h_out = static_cast<uint16_t*>(h_out); a.rceil = mode == MX_RCEIL;
+  return launched(mxk::launch_gemm_grouped_swiglu(a, as_stream(stream)), fn);
+}
+
 // Token-order variants: the output holds the T routed tokens, not the
 // padded rows.
 static mx_status grouped_2d3d_unpad(const char* fn, const uint8_t* qa, const uint8_t* sa, const uint8_t* qw,

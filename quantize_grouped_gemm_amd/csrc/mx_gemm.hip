@@ -47,6 +47,7 @@
 
 #include "mx_device.h"
 #include "mx_kernels.h"
+#include "mx_tile.h"
 
 namespace mxk {
 
@@ -84,6 +85,10 @@ struct TileSpec {
   void* out;             // C(0, 0) of the tile
   int64_t ldo;
   bool out_f32;
+  // B rows 128..255 of the tile sit b_hi rows further down B, and the
+  // output columns of its second column half out_hi columns further right
+  // (the fused SwiGLU tile: gate and up halves of one block of h)
+  int64_t b_hi = 0, out_hi = 0;
 };
 
 template <int OPSEL>
@@ -124,7 +129,8 @@ __device__ __forceinline__ void store_tile_t(const v16f (&acc)[4][4], const Tile
   const bool full = ts.valid_m == kBM && ts.valid_n == kBN;
   const int64_t rs = ts.ldo * esz;   // bytes per output row
   const int lrow = lane >> 5, col = 4 * (lane & 31);
-  uint8_t* base = reinterpret_cast<uint8_t*>(ts.out) + (int64_t)(wm * 128 + lrow) * rs + (wn * 128 + col) * esz;
+  uint8_t* base =
+      reinterpret_cast<uint8_t*>(ts.out) + (int64_t)(wm * 128 + lrow) * rs + (wn * (128 + ts.out_hi) + col) * esz;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -210,6 +216,8 @@ __device__ __forceinline__ TileSpec uniform_spec(const TileSpec& t) {
   u.out = uniform_ptr(t.out);
   u.ldo = uniform_i64(t.ldo);
   u.out_f32 = uniform_i32(t.out_f32) != 0;
+  u.b_hi = uniform_i64(t.b_hi);
+  u.out_hi = uniform_i64(t.out_hi);
   return u;
 }
 
@@ -233,7 +241,7 @@ __device__ __forceinline__ void store_tile_direct(const v16f (&acc)[4][4], const
   const uint32_t rs = (uint32_t)ts.ldo * (F32 ? 4u : 2u);   // row pitch in bytes
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(ts.out), (short)0, 0x7FFFFFFF, 0x00020000);
   if constexpr (F32) {
-    const uint32_t voff = (uint32_t)(wm * 128 + 4 * h) * rs + (uint32_t)(wn * 128 + c) * 4u;
+    const uint32_t voff = (uint32_t)(wm * 128 + 4 * h) * rs + (uint32_t)(wn * (128 + ts.out_hi) + c) * 4u;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -246,7 +254,8 @@ __device__ __forceinline__ void store_tile_direct(const v16f (&acc)[4][4], const
   } else {
     // selections by mask arithmetic: the registers are indexed statically
     const uint32_t om = 0u - (uint32_t)(lane & 1);   // all ones on odd lanes
-    const uint32_t voff = (uint32_t)(wm * 128 + 4 * h + (lane & 1)) * rs + (uint32_t)(wn * 128 + (c & ~1)) * 2u;
+    const uint32_t voff =
+        (uint32_t)(wm * 128 + 4 * h + (lane & 1)) * rs + (uint32_t)(wn * (128 + ts.out_hi) + (c & ~1)) * 2u;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -355,6 +364,7 @@ struct TileDma {
   uint32_t voff_pa, voff_pb;   // prefetch: this lane's row of the tile's A / B prefetch share
   uint32_t lda, ldb, sstep_a, sstep_b;
   uint32_t k_begin;
+  uint32_t brow_add;   // rows added to this wave's B rows (b_hi for the tile's second half)
   int wu;
 };
 
@@ -376,7 +386,7 @@ __device__ __forceinline__ void issue_step(const TileDma& d, int ks, uint8_t* st
     __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (__attribute__((address_space(3))) void*)rows, 16,
                                              d.voff_a[i & 1], row0 * d.lda + kb, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rb, (__attribute__((address_space(3))) void*)(rows + kStageA), 16,
-                                             d.voff_b[i & 1], row0 * d.ldb + kb, 0, 0);
+                                             d.voff_b[i & 1], (row0 + d.brow_add) * d.ldb + kb, 0, 0);
   }
   uint8_t* sdst = st + kStageA + kStageB + 64 * d.wu * 4;
   const uint32_t lane4 = (threadIdx.x & 63) * 4;
@@ -384,7 +394,7 @@ __device__ __forceinline__ void issue_step(const TileDma& d, int ks, uint8_t* st
   __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsa, (__attribute__((address_space(3))) void*)sdst, 4, lane4,
                                            kstep * d.sstep_a + 256 * d.wu, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsb, (__attribute__((address_space(3))) void*)(sdst + kBM * 4), 4,
-                                           lane4, kstep * d.sstep_b + 256 * d.wu, 0, 0);
+                                           lane4, kstep * d.sstep_b + 4 * (64 * d.wu + d.brow_add), 0, 0);
 }
 
 // L2 prefetch of K step ks: one 4-byte load per lane per operand touches
@@ -474,14 +484,116 @@ __device__ __forceinline__ void step_full(const TileDma& d, int ks, int nk, uint
   }
 }
 
-__device__ __forceinline__ void gemm_tile(const TileSpec& tile) {
+// LDS writes of this wave are done, then a workgroup barrier (without the
+// wait for outstanding global stores that a full __syncthreads implies).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  wg_barrier();
+}
+
+// Outputs of the fused SwiGLU epilogue (the w13 forward of the grouped MLP).
+struct SwigluOut {
+  uint8_t *q_row, *s_row, *q_col, *s_col;   // h quantized both ways, k128 scales
+  uint16_t* h;                              // bf16 h, or null
+  int64_t rows, hidden;                     // h is [rows, hidden]
+  bool rceil;
+};
+
+// Fused SwiGLU + dual MX quantization of one tile of the w13 forward. The
+// tile's first 128 columns are the gate a = z[:, c0 .. c0 + 127] and its last
+// 128 the matching up columns b = z[:, H + c0 ..] (z itself is stored by the
+// caller). Every h element is formed exactly as the standalone SwiGLU kernel
+// forms it: from the bf16-rounded a and b, in float32, rounded to bf16; and
+// it is quantized by the same tile routines, so the codes are the same bytes.
+//   1. The up waves (wn = 1) pass their bf16 values to the gate waves of the
+//      same rows through LDS, in register order (both hold the MFMA layout).
+//   2. The gate waves form h and write it to LDS as a [256][128] bf16 tile;
+//      neighbouring lanes swap one value so each write is a whole dword.
+//   3. All 256 threads quantize the two 128 x 128 halves of that tile.
+// Rows past valid_m belong to the next group and are left alone.
+__device__ __forceinline__ void swiglu_epilogue(const v16f (&acc)[4][4], const SwigluOut& o, int valid_m,
+                                                int64_t r0, int64_t c0, uint8_t* lds_x, uint8_t* lds_y) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  uint32_t* X = reinterpret_cast<uint32_t*>(lds_x);   // [2][128 pairs][64 lanes] bf16 pairs of b
+  uint32_t* Y = reinterpret_cast<uint32_t*>(lds_y);   // [256][64] dwords: h rows of 128 bf16
+  lds_barrier();   // every wave is done with the stage buffers
+  if (wn == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          X[(wm * 128 + (i * 4 + j) * 8 + q) * 64 + lane] = pack_bf16x2(acc[i][j][2 * q], acc[i][j][2 * q + 1]);
+  }
+  lds_barrier();
+  if (wn == 0) {
+    const uint32_t om = 0u - (uint32_t)(lane & 1);   // all ones on odd lanes
+    const int h = lane >> 5, c = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t bp = X[(wm * 128 + (i * 4 + j) * 8 + q) * 64 + lane];
+          const uint32_t ap = pack_bf16x2(acc[i][j][2 * q], acc[i][j][2 * q + 1]);
+          const uint32_t h0 = f32_to_bf16(swiglu_f32(bf16_lo(ap), bf16_lo(bp)));   // row k = 2q
+          const uint32_t h1 = f32_to_bf16(swiglu_f32(bf16_hi(ap), bf16_hi(bp)));   // row k + 1
+          // even lanes: columns c, c + 1 of row k; odd lanes: c - 1, c of row k + 1
+          const uint32_t send = h1 ^ ((h0 ^ h1) & om);
+          const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true) & 0xFFFFu;
+          const uint32_t lo = h0 ^ ((h0 ^ got) & om);
+          const uint32_t hi = got ^ ((got ^ h1) & om);
+          const int row = wm * 128 + 32 * i + 8 * (q >> 1) + 4 * h + 2 * (q & 1) + (lane & 1);
+          Y[row * 64 + ((32 * j + c) >> 1)] = lo | (hi << 16);
+        }
+  }
+  lds_barrier();
+  uint4* Q = reinterpret_cast<uint4*>(lds_x);   // the quantizer's LDS tile; b is no longer needed
+  const int t = threadIdx.x, cc = t & 15;
+  for (int s = 0; s < 2; ++s) {
+    const int rv = min(kTR, valid_m - kTR * s);
+    if (rv <= 0) break;
+    uint4 v[kTileChunks];
+#pragma unroll
+    for (int jj = 0; jj < kTileChunks; ++jj) {
+      const int row = (t >> 4) + 16 * jj;
+      v[jj] = *reinterpret_cast<const uint4*>(&Y[(kTR * s + row) * 64 + 4 * cc]);
+    }
+    const int64_t rs0 = r0 + kTR * s;
+    if (o.h) {
+#pragma unroll
+      for (int jj = 0; jj < kTileChunks; ++jj) {
+        const int row = (t >> 4) + 16 * jj;
+        if (row < rv) *reinterpret_cast<uint4*>(o.h + (rs0 + row) * o.hidden + c0 + 8 * cc) = v[jj];
+      }
+    }
+    if (o.q_row) tile_rowq(v, rv, kTC, o.rceil, TileOut{o.q_row, o.s_row, o.hidden, o.rows, true}, rs0, c0);
+    if (o.q_col) {
+      tile_to_lds(v, Q);
+      lds_barrier();
+      tile_colq(Q, rv, kTC, o.rceil, TileOut{o.q_col, o.s_col, o.rows, o.hidden, true}, rs0, c0);
+      lds_barrier();   // before the next half overwrites Q
+    }
+  }
+}
+
+// FUSED: the tile is a fused SwiGLU tile (see swiglu_epilogue); a tile
+// without K steps (the tail) then still runs the epilogue on zeros.
+template <bool FUSED = false>
+__device__ __forceinline__ void gemm_tile(const TileSpec& tile, const SwigluOut* so = nullptr, int64_t h_r0 = 0,
+                                          int64_t h_c0 = 0) {
   const TileSpec ts = uniform_spec(tile);
   __shared__ __align__(16) uint8_t st0[kStageBytes];
   __shared__ __align__(16) uint8_t st1[kStageBytes];
   __shared__ __align__(16) uint8_t sink[256];
-  if (ts.nk <= 0) {
-    zero_tile(ts);
-    return;
+  if constexpr (!FUSED) {
+    if (ts.nk <= 0) {
+      zero_tile(ts);
+      return;
+    }
   }
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -489,9 +601,11 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& tile) {
 
   TileDma d;
   d.wu = __builtin_amdgcn_readfirstlane(w);
+  d.brow_add = d.wu >= 2 ? (uint32_t)ts.b_hi : 0u;
   // each buffer resource ends after the last valid row: rows past it read 0
   d.ra = __builtin_amdgcn_make_buffer_rsrc((void*)ts.a, (short)0, (int)(ts.valid_m * ts.lda), 0x00020000);
-  d.rb = __builtin_amdgcn_make_buffer_rsrc((void*)ts.b, (short)0, (int)(ts.valid_n * ts.ldb), 0x00020000);
+  d.rb = __builtin_amdgcn_make_buffer_rsrc((void*)ts.b, (short)0, (int)((ts.valid_n + ts.b_hi) * ts.ldb),
+                                           0x00020000);
   // scale rows past the valid ones hold other rows' scales (or read 0 past
   // the end of the matrix): they only meet zero operand rows, whose
   // outputs are not stored
@@ -511,7 +625,10 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& tile) {
   // the 256 lanes of the workgroup spread over the share's rows
   const uint32_t t = threadIdx.x;
   d.voff_pa = (uint32_t)(ts.pf_a0 + ((t * (uint32_t)ts.pf_an) >> 8)) * d.lda;
-  d.voff_pb = (uint32_t)(ts.pf_b0 + ((t * (uint32_t)ts.pf_bn) >> 8)) * d.ldb;
+  {
+    const uint32_t prow = (uint32_t)(ts.pf_b0 + ((t * (uint32_t)ts.pf_bn) >> 8));
+    d.voff_pb = (prow + (prow >= 128 ? (uint32_t)ts.b_hi : 0u)) * d.ldb;
+  }
 
   v16f acc[4][4];
 #pragma unroll
@@ -520,6 +637,7 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& tile) {
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
   const int nk = ts.nk;
+  if (!FUSED || nk > 0) {
   const int last = nk - 1;
   // prologue: steps 0 and 1 to LDS, each DMA followed by two prefetch loads
   // (steps 2 and 3; past the end, the last step stands in)
@@ -541,16 +659,18 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& tile) {
   }
   if (ks < nk) step_full(d, ks, nk, st0, st1, r, acc, wm, wn, lane, sink);
   MX_WAIT_VM_LDS(0);
+  }
   if (direct_epilogue(ts)) {
     if (ts.out_f32)
       store_tile_direct<true>(acc, ts);
     else
       store_tile_direct<false>(acc, ts);
-    return;
+  } else {
+    wg_barrier();   // every wave is done with the stage buffers
+    uint8_t* mine = (w & 1 ? st1 : st0) + (w >> 1) * kEpiWaveBytes;
+    store_tile(acc, ts, mine);
   }
-  wg_barrier();   // every wave is done with the stage buffers
-  uint8_t* mine = (w & 1 ? st1 : st0) + (w >> 1) * kEpiWaveBytes;
-  store_tile(acc, ts, mine);
+  if constexpr (FUSED) swiglu_epilogue(acc, *so, ts.valid_m, h_r0, h_c0, st1, st0);
 }
 
 // ---------------------------------------------------------------- bf16 wgrad
@@ -870,6 +990,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dense(GemmArgs a) {
 // ceil(r / 256) tiles; the last may hold only 128 rows), followed by the
 // tiles of the tail [ends[E-1], Tcap), which are written as zeros. The grid
 // is an upper bound on row tiles x column tiles; surplus workgroups exit.
+// FUSED: the w13 forward with SwiGLU + dual quantization in the epilogue.
+// Its tile t covers h columns [128 t, 128 t + 128): B rows [128 t, + 128) of
+// the expert's w13 (gate) and [H + 128 t, + 128) (up); z columns likewise.
+template <bool FUSED>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   __shared__ int32_t ends[kMaxGroups + 1];
   __shared__ int32_t tile_end[kMaxGroups + 1];   // inclusive prefix of row-tile counts
@@ -927,7 +1051,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   __syncthreads();
   const int mt = tile_end[a.E];            // row tiles, the tail's included
   const int mt_groups = tile_end[a.E - 1]; // row tiles of the groups
-  const int nt = (int)((a.N + kBN - 1) / kBN);
+  const int64_t H = a.N / 2;   // FUSED: z is [Tcap, 2H]
+  const int nt = FUSED ? (int)(H / 128) : (int)((a.N + kBN - 1) / kBN);
   const int b = (int)blockIdx.x;
   // the groups' tiles are dealt to the XCDs in chunks; the tail's zero tiles
   // follow the span of that deal, so no XCD's share is padded with them
@@ -955,7 +1080,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   const int first = g == 0 ? 0 : tile_end[g - 1];
   const int64_t gs = group_start(ends, g);
   const int64_t m0 = gs + (int64_t)(tile - first) * kBM;
-  const int64_t n0 = (int64_t)tn * kBN;
+  const int64_t n0 = FUSED ? (int64_t)tn * 128 : (int64_t)tn * kBN;
   TileSpec ts;
   const int gb = min(g, a.E - 1);
   const int64_t steps = a.K / kBK;
@@ -970,9 +1095,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   ts.sbytes_a = steps * ts.sstep_a - m0 * 4;
   ts.sbytes_b = steps * ts.sstep_b - n0 * 4;
   ts.valid_m = (int)min<int64_t>(kBM, ends[g] - m0);
-  ts.valid_n = (int)min<int64_t>(kBN, a.N - n0);
+  ts.valid_n = FUSED ? kBN : (int)min<int64_t>(kBN, a.N - n0);
   ts.k_begin = 0;
   ts.nk = g < a.E ? (int)(a.K / kBK) : 0;
+  if constexpr (FUSED) {
+    ts.b_hi = H - 128;
+    ts.out_hi = H - 128;
+  }
   int64_t out_row = m0;
   if (a.sizes) {
     // token order: only the group's real rows, shifted to its token range
@@ -994,7 +1123,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   ts.out = reinterpret_cast<uint8_t*>(a.out) + (out_row * a.ldo + n0) * esz;
   ts.ldo = a.ldo;
   ts.out_f32 = a.out_f32;
-  gemm_tile(ts);
+  if constexpr (FUSED) {
+    const SwigluOut so{a.hq_row, a.hs_row, a.hq_col, a.hs_col, a.h_out, a.M, H, a.rceil};
+    gemm_tile<true>(ts, &so, m0, n0);
+  } else {
+    gemm_tile(ts);
+  }
 }
 
 // The grid covers E x (N tiles) x (K tiles) of dW. Tile indices run over the
@@ -1079,7 +1213,14 @@ hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) {
   // the chunked deal of the groups' tiles spans at most 8 * kXcdChunk - 1
   // indices more than the tiles themselves
   const int64_t tiles = mtiles * ((a.N + kBN - 1) / kBN) + 8 * kXcdChunk;
-  hipLaunchKernelGGL(k_gemm_grouped, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a);
+  hipLaunchKernelGGL(k_gemm_grouped<false>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_grouped_swiglu(const GemmArgs& a, hipStream_t s) {
+  const int64_t mtiles = a.M / kBM + (a.E + 2) / 2 + 1;
+  const int64_t tiles = mtiles * (a.N / 2 / 128) + 8 * kXcdChunk;
+  hipLaunchKernelGGL(k_gemm_grouped<true>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -65,6 +65,11 @@ struct GemmArgs {
   // rows and the tail are not written. out has out_rows rows.
   const int32_t* sizes = nullptr;
   int64_t out_rows = 0;
+  // grouped w13 forward with fused SwiGLU (N = 2H): h = silu(z[:, :H]) *
+  // z[:, H:] quantized both ways (k128 scales), bf16 h optional
+  uint8_t *hq_row = nullptr, *hs_row = nullptr, *hq_col = nullptr, *hs_col = nullptr;
+  uint16_t* h_out = nullptr;
+  bool rceil = true;
 };
 
 struct PadArgs {
@@ -93,6 +98,7 @@ hipError_t launch_swiglu_bwd(const SwigluBwdArgs& a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_grouped_swiglu(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_wgrad(const GemmArgs& a, hipStream_t s);
 // bf16 wgrad_with_hp: qa / qb are G [M = Tcap, N] and X [Tcap, K] bf16,
 // lda / ldb their row pitches in bytes, out bf16 [E, N, K].

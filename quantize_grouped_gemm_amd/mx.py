@@ -44,6 +44,8 @@ _SIGS = {
                                  ctypes.c_int),
     "mx_scaled_grouped_mm_dgrad": ([_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P],
                                    ctypes.c_int),
+    "mx_scaled_grouped_mm_swiglu_fwd": ([_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _P,
+                                         _P, _P, _P, _P], ctypes.c_int),
     "mx_scaled_grouped_mm_fwd_unpad": ([_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, ctypes.c_int, _P,
                                         _P, _P], ctypes.c_int),
     "mx_scaled_grouped_mm_dgrad_unpad": ([_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, ctypes.c_int, _P,
@@ -212,6 +214,30 @@ def grouped_mm_fwd(qa, sa, qw, sw, offs, out_dtype=torch.bfloat16, out=None, dev
 
 def grouped_mm_dgrad(qa, sa, qw, sw, offs, out_dtype=torch.bfloat16, out=None, dev_err=None):
     return _grouped("mx_scaled_grouped_mm_dgrad", qa, sa, qw, sw, offs, out_dtype, out, dev_err)
+
+
+def grouped_mm_swiglu_fwd(qa, sa, qw13, sw13, offs, mode="rceil", want_h=False, out=None, dev_err=None):
+    """The w13 grouped forward fused with SwiGLU + dual quantization.
+    qw13 [E, 2H, K] (gate rows first). Returns dict with z [Tcap, 2H] bf16,
+    q_row/s_row, q_col/s_col of h (k128 scales) and, if asked, h bf16."""
+    Tcap, K = qa.shape
+    E, H2 = qw13.shape[0], qw13.shape[1]
+    H = H2 // 2
+    dev = qa.device
+    out = dict(out or {})
+    out.setdefault("z", torch.empty((Tcap, H2), dtype=torch.bfloat16, device=dev))
+    out.setdefault("q_row", _u8((Tcap, H), dev))
+    out.setdefault("s_row", _u8(scale_shape(Tcap, H), dev))
+    out.setdefault("q_col", _u8((H, Tcap), dev))
+    out.setdefault("s_col", _u8(scale_shape(H, Tcap), dev))
+    if want_h:
+        out.setdefault("h", torch.empty((Tcap, H), dtype=torch.bfloat16, device=dev))
+    st = lib().mx_scaled_grouped_mm_swiglu_fwd(_ptr(qa), _ptr(sa), _ptr(qw13), _ptr(sw13), _ptr(offs), E, Tcap, H,
+                                               K, _MODES[mode], _ptr(out["z"]), _ptr(out["q_row"]),
+                                               _ptr(out["s_row"]), _ptr(out["q_col"]), _ptr(out["s_col"]),
+                                               _ptr(out.get("h")), _ptr(dev_err), _stream(dev))
+    _check(st, "mx_scaled_grouped_mm_swiglu_fwd")
+    return out
 
 
 def _grouped_unpad(name, qa, sa, qw, sw, offs, sizes, T, out_dtype, out, dev_err):

@@ -30,7 +30,7 @@ def _declared():
 def test_header_symbols_exported_and_bound():
     L = _lib()
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(L, n), n
     assert sorted(mx.EXPORTS) == names
@@ -64,6 +64,11 @@ def test_argument_errors_are_reported_without_device_work():
     assert L.mx_scaled_grouped_mm_wgrad(p, p, p, p, p, 0, 128, 64, 64, 1, p, None, None) == 2
     assert L.mx_pad_groups(p, p, 2, 10, 24, 128, 256, p, p, p, None, None) == 2
     assert L.mx_unpad_groups(p, p, 128, 10, 32, None, None) == 1
+    # fused w13 + SwiGLU: H not a multiple of 128, bad mode
+    assert L.mx_scaled_grouped_mm_swiglu_fwd(p, p, p, p, p, 4, 256, 96, 128, 0, p, p, p, p, p, None, None,
+                                             None) == 2
+    assert L.mx_scaled_grouped_mm_swiglu_fwd(p, p, p, p, p, 4, 256, 128, 128, 5, p, p, p, p, p, None, None,
+                                             None) == 4
     # token-order grouped GEMM: T beyond Tcap, missing group sizes
     assert L.mx_scaled_grouped_mm_fwd_unpad(p, p, p, p, p, p, 4, 256, 300, 64, 128, 0, p, None, None) == 2
     assert L.mx_scaled_grouped_mm_dgrad_unpad(p, p, p, p, p, None, 4, 256, 200, 64, 128, 0, p, None, None) == 1

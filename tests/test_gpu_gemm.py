@@ -440,3 +440,48 @@ def test_dsv3_full_size_sampled(gpu):
             worst, strict = bf16_ulp_check(bf16_host(got[e][rows][:, cols]), ref[e])
             assert worst <= 2.0, f"hp wgrad group {e}: {worst} ulp"
         start = end
+
+
+@pytest.mark.parametrize("mode", ["rceil", "floor"])
+@pytest.mark.parametrize("sizes,H,K", [([250, 0, 300, 50], 256, 256), ([128, 256, 1], 384, 128),
+                                       ([0, 0, 5], 128, 256), ([700, 0, 0, 300, 129], 256, 384)])
+def test_grouped_swiglu_fused_equals_unfused(gpu, mode, sizes, H, K):
+    """The w13 forward with the SwiGLU + dual quantization in its epilogue
+    writes the same z, the same h and the same h codes and scales (both
+    directions) as the grouped forward followed by the standalone fused
+    SwiGLU kernel, including pad rows, the tail and empty groups."""
+    sizes = np.array(sizes, np.int32)
+    E, T = len(sizes), int(sizes.sum())
+    Tcap = synth.capacity(T, E)
+    offs = _offsets(-(-sizes // 128) * 128)
+    g = synth.generator(T + H + K, dev())
+    x = synth.normal_bf16((Tcap, K), 1.0, g, dev())
+    w13 = synth.normal_bf16((E, 2 * H, K), 0.05, g, dev())
+    qx, qw = mx.quantize(x, mode), mx.quantize(w13, mode)
+    offs_d = to_dev(offs)
+    fused = mx.grouped_mm_swiglu_fwd(qx["q_row"], qx["s_row"], qw["q_row"], qw["s_row"], offs_d, mode,
+                                     want_h=True)
+    z = mx.grouped_mm_fwd(qx["q_row"], qx["s_row"], qw["q_row"], qw["s_row"], offs_d, torch.bfloat16)
+    ref = mx.swiglu_quant_fwd(z[:, :H], z[:, H:], mode, want_h=True)
+    assert torch.equal(fused["z"], z)
+    for k in ("h", "q_row", "s_row", "q_col", "s_col"):
+        assert torch.equal(fused[k], ref[k]), k
+
+
+def test_grouped_swiglu_fused_full_size(gpu):
+    """The MoE Scout w13 forward (Tcap 18432, 16 experts, D 5120, H 8192)
+    fused with its SwiGLU: the same bytes as the unfused pair."""
+    E, Tcap, offs = _moe_scout_groups()
+    H, K = 8192, 5120
+    g = synth.generator(15, dev())
+    x = synth.normal_bf16((Tcap, K), 1.0, g, dev())
+    w13 = synth.normal_bf16((E, 2 * H, K), 0.02, g, dev())
+    qx, qw = mx.quantize(x, "rceil"), mx.quantize(w13, "rceil")
+    del w13
+    offs_d = to_dev(offs)
+    fused = mx.grouped_mm_swiglu_fwd(qx["q_row"], qx["s_row"], qw["q_row"], qw["s_row"], offs_d)
+    z = mx.grouped_mm_fwd(qx["q_row"], qx["s_row"], qw["q_row"], qw["s_row"], offs_d, torch.bfloat16)
+    assert torch.equal(fused["z"], z)
+    ref = mx.swiglu_quant_fwd(z[:, :H], z[:, H:], "rceil")
+    for k in ("q_row", "s_row", "q_col", "s_col"):
+        assert torch.equal(fused[k], ref[k]), k
