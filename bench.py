@@ -40,7 +40,8 @@ WORKLOADS = ("moe_scout", "moe_dsv3", "moe_dsv3_hp", "dense", "quant", "linear",
 # sources are the ones the counters were taken on.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_grouped_moe_scout_traffic.md")
 GEMM_SOURCES = ("quantize_grouped_gemm_amd/csrc/mx_gemm.hip", "quantize_grouped_gemm_amd/csrc/mx_kernels.h",
-                "quantize_grouped_gemm_amd/csrc/mx_device.h", "quantize_grouped_gemm_amd/build.py")
+                "quantize_grouped_gemm_amd/csrc/mx_device.h", "quantize_grouped_gemm_amd/csrc/mx_tile.h",
+                "quantize_grouped_gemm_amd/build.py")
 
 
 def gemm_source_hash():
