@@ -52,6 +52,7 @@ __all__ = [
     "BLOCK", "E4M3_MAX", "RCEIL", "FLOOR", "E4M3_VALUES",
     "bf16_to_f64", "f64_to_bf16", "f64_to_f32", "e8m0_to_f64",
     "scale_exponent", "e4m3_encode", "quantize", "quantize_bf16",
+    "quantize_fp8_rows", "quantize_fp8_bf16",
     "dequantize", "silu", "swiglu_f64", "swiglu_grad_f64", "swiglu_fwd",
     "swiglu_bwd",
     "swiglu_quant_fwd", "swiglu_quant_bwd", "scaled_mm", "grouped_mm",
@@ -221,6 +222,67 @@ def quantize_bf16(bits, mode, rowwise=True, colwise=False):
         out["q_row"], out["s_row"] = quantize(x, mode)
     if colwise:
         out["q_col"], out["s_col"] = quantize(np.swapaxes(x, -1, -2), mode)
+    return out
+
+
+# --------------------------------------------------------------------------
+# FP8 with one scale per row (the non-MX FP8 grouped-mm training variant;
+# [P1], review thread: FP8GroupedMMConfig; [P2], Autograd func changes: FP8
+# MoE training, about 10% more tokens/s on Llama4 Scout. Its scaling is not
+# on the pages.)
+# --------------------------------------------------------------------------
+
+def quantize_fp8_rows(x):
+    """READING: FP8 E4M3 with one power-of-two scale per row of the quantized
+    (last) axis, chosen by the RCEIL rule over the whole row: the smallest E
+    with amax(row) <= 448 * 2**E, so nothing saturates; elements are encoded
+    as in ``quantize``; a row holding a NaN or infinity gets scale 0xFF and
+    codes 0x7F with the element's sign. The row's scale byte is returned once
+    per 32-block, so the result is an MX operand whose block scales along a
+    row are all equal (the MX GEMMs then compute the FP8 row-scaled GEMM).
+    Returns (codes uint8 [..., C], scales uint8 [..., C/32])."""
+    x = np.asarray(x, np.float64)
+    C = x.shape[-1]
+    if C % BLOCK:
+        raise ValueError("quantized axis must be a multiple of 32")
+    with np.errstate(invalid="ignore"):
+        amax = np.max(np.abs(x), axis=-1)
+    finite = np.isfinite(amax)
+    E = scale_exponent(np.where(finite, amax, 0.0), RCEIL)
+    y = x * np.ldexp(1.0, -E)[..., None]
+    codes = e4m3_encode(np.where(finite[..., None], y, 0.0))
+    bad = (np.signbit(x).astype(np.uint8) << 7) | np.uint8(0x7F)
+    codes = np.where(finite[..., None], codes, bad).astype(np.uint8)
+    sb = np.where(finite, E + E8M0_BIAS, 255).astype(np.uint8)
+    return codes, np.repeat(sb[..., None], C // BLOCK, axis=-1)
+
+
+def quantize_fp8_bf16(bits, rowwise=True, colwise=False, segments=None):
+    """FP8 row-scaled quantization of a bf16 tensor [..., R, C]: row-wise
+    scales one per row of [R, C]; column-wise quantizes the transpose
+    [..., C, R] one scale per row of it, or, with ``segments`` (exclusive ends
+    along R, the grouped GEMM offsets; READING: the weight gradient's
+    contraction runs over each group's own tokens, so each column gets one
+    scale per group), one scale per (column, segment); rows past the last end
+    form a segment of their own. Returns a dict with q_row, s_row, q_col,
+    s_col as requested (MX-style layouts)."""
+    x = bf16_to_f64(bits)
+    out = {}
+    if rowwise:
+        out["q_row"], out["s_row"] = quantize_fp8_rows(x)
+    if colwise:
+        xt = np.swapaxes(x, -1, -2)
+        if segments is None:
+            out["q_col"], out["s_col"] = quantize_fp8_rows(xt)
+        else:
+            R = xt.shape[-1]
+            q = np.zeros(xt.shape, np.uint8)
+            sc = np.zeros(xt.shape[:-1] + (R // BLOCK,), np.uint8)
+            bounds = [0] + [int(e) for e in segments] + [R]
+            for s, e in zip(bounds[:-1], bounds[1:]):
+                if e > s:
+                    q[..., s:e], sc[..., s // BLOCK:e // BLOCK] = quantize_fp8_rows(xt[..., s:e])
+            out["q_col"], out["s_col"] = q, sc
     return out
 
 

@@ -125,3 +125,80 @@ def test_dequantize_is_exact_product():
     for r in range(8):
         for c in range(64):
             assert d[r, c] == mx.E4M3_VALUES[q[r, c]] * 2.0 ** (int(s[r, c // 32]) - 127)
+
+
+# ---------------------------------------------------------------- FP8 row-scaled
+
+def _fp8_rows_brute(x):
+    """One scale per row by direct search: the smallest integer E in the E8M0
+    range with every |x| <= 448 * 2**E; codes by torch's own float8 cast of
+    x * 2**-E (exact in float32 for these inputs)."""
+    import torch
+    x = np.asarray(x, np.float64)
+    R, C = x.shape
+    q = np.zeros((R, C), np.uint8)
+    sc = np.zeros((R, C // 32), np.uint8)
+    for r in range(R):
+        amax = np.max(np.abs(x[r]))
+        E = -127
+        while E < 127 and amax > 448.0 * 2.0 ** E:
+            E += 1
+        y = torch.from_numpy((x[r] * 2.0 ** -E).astype(np.float32))
+        q[r] = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        sc[r] = E + 127
+    return q, sc
+
+
+def test_fp8_rows_against_brute_force_and_torch_cast():
+    rng = np.random.default_rng(11)
+    bits = _rand_bf16((24, 96), 11)
+    x = mx.bf16_to_f64(bits)
+    x[3] *= 2.0 ** -120            # near the bottom of the scale range
+    x[4] *= 2.0 ** 100             # near the top
+    x[5] = 0.0                     # amax 0
+    x[6, 7] = 448.0 * 2.0 ** 3     # amax exactly on a power-of-two bound
+    x[7] = rng.choice([-1.0, 1.0], 96) * 2.0 ** rng.integers(-20, 20, 96)
+    q, sc = mx.quantize_fp8_rows(x)
+    bq, bsc = _fp8_rows_brute(x)
+    np.testing.assert_array_equal(sc, bsc)
+    np.testing.assert_array_equal(q, bq)
+
+
+def test_fp8_rows_reduce_to_mx_when_every_block_holds_the_row_max():
+    """With the row's largest magnitude present in every 32-block, the row
+    scale and each MX block scale (RCEIL) coincide, so the bytes are the MX
+    quantization's."""
+    bits = _rand_bf16((16, 128), 12)
+    x = mx.bf16_to_f64(bits)
+    amax = np.max(np.abs(x), axis=1, keepdims=True)
+    x[:, ::32] = amax          # plant the row max at the start of every block
+    q, sc = mx.quantize_fp8_rows(x)
+    mq, msc = mx.quantize(x, "rceil")
+    np.testing.assert_array_equal(q, mq)
+    np.testing.assert_array_equal(sc, msc)
+    # and a row whose blocks differ gets one scale for all of them
+    y = x.copy()
+    y[0, 40] = amax[0, 0] * 64
+    q2, sc2 = mx.quantize_fp8_rows(y)
+    assert len(set(sc2[0].tolist())) == 1 and sc2[0, 0] == sc[0, 0] + 6
+
+
+def test_fp8_columns_by_segment_and_nonfinite_rows():
+    bits = _rand_bf16((384, 64), 13)
+    seg = np.array([128, 128, 256])           # an empty segment, then a tail of 128
+    out = mx.quantize_fp8_bf16(bits, rowwise=False, colwise=True, segments=seg)
+    x = mx.bf16_to_f64(bits)
+    for s, e in ((0, 128), (128, 256), (256, 384)):
+        q, sc = mx.quantize_fp8_rows(x[s:e].T)
+        np.testing.assert_array_equal(out["q_col"][:, s:e], q)
+        np.testing.assert_array_equal(out["s_col"][:, s // 32:e // 32], sc)
+    whole = mx.quantize_fp8_bf16(bits, rowwise=True, colwise=True)
+    np.testing.assert_array_equal(whole["q_col"], mx.quantize_fp8_rows(x.T)[0])
+    np.testing.assert_array_equal(whole["q_row"], mx.quantize_fp8_rows(x)[0])
+    z = x[:2].copy()
+    z[0, 5] = np.nan
+    z[1, 9] = -np.inf
+    q, sc = mx.quantize_fp8_rows(z)
+    assert np.all(sc == 255)
+    np.testing.assert_array_equal(q & 0x7F, 0x7F)
+    np.testing.assert_array_equal(q >> 7, np.signbit(z).astype(np.uint8))
