@@ -94,11 +94,15 @@ def _build_workload(name, torch, dev):
     import numpy as np
     from quantize_grouped_gemm_amd import mlp, synth
     if name.startswith("moe"):
-        if name == "moe_scout":
+        recipe = "mxfp8"
+        if name in ("moe_scout", "moe_scout_fp8"):
             c = synth.MOE_SCOUT
             sizes = synth.zipf_group_sizes(c["T"], c["E"], 14)
             wgrad = "mx"
             desc = "Llama4-Scout-like routed experts, one GPU's share"
+            if name == "moe_scout_fp8":
+                recipe = "fp8_rowwise"
+                desc += ", FP8 with one scale per row"
         else:
             c = synth.MOE_DSV3
             sizes = synth.dirichlet_group_sizes(c["T"], c["E"], 0.3)
@@ -110,9 +114,10 @@ def _build_workload(name, torch, dev):
         w13 = torch.cat([w1, w3], dim=1)
         del w1, w3
         sizes_d = torch.from_numpy(sizes.astype(np.int32)).to(dev)
-        net = mlp.MoEMLP(E, T, D, H, Tcap, dev, wgrad=wgrad)
+        net = mlp.MoEMLP(E, T, D, H, Tcap, dev, wgrad=wgrad, recipe=recipe)
         args = (x, sizes_d, w13, w2, dy)
-        config = {"workload": f"{name}: MXFP8 SwiGLU MoE MLP fwd+bwd, E={E} D={D} H={H} T={T} "
+        fmt = "FP8 row-scaled" if recipe == "fp8_rowwise" else "MXFP8"
+        config = {"workload": f"{name}: {fmt} SwiGLU MoE MLP fwd+bwd, E={E} D={D} H={H} T={T} "
                               f"(padded to 128, Tcap={Tcap}), wgrad={'bf16 wgrad_with_hp' if wgrad == 'hp' else 'mxfp8'}",
                   "experts": E, "dim": D, "hidden": H, "tokens": T, "capacity": Tcap,
                   "group_sizes": [int(v) for v in sizes], "scale_mode": "rceil", "description": desc}
@@ -378,6 +383,14 @@ def main():
                 "workload": c2["workload"] + "; 4 micro-batches per optimizer step, expert weights "
                                               "dual-quantized once and reused"}
             del n2, a2, s2, acc
+            torch.cuda.empty_cache()
+        if name == "moe_scout":
+            # the FP8 row-scaled recipe of the same step
+            n2, a2, s2, tok2, c2 = _build_workload("moe_scout_fp8", torch, dev)
+            w2_, p2 = _time_stages(s2, max(3, args.steps // 2), 2, torch)
+            comp["moe_scout_fp8_rowwise"] = {"tokens_per_s": round(tok2 / w2_, 1), "ms_per_step": round(w2_ * 1e3, 3),
+                                             "kernels": _kernel_table(s2, p2)[0], "workload": c2["workload"]}
+            del n2, a2, s2
             torch.cuda.empty_cache()
         for other in ("dense", "moe_dsv3", "moe_dsv3_hp"):
             n2, a2, s2, tok2, c2 = _build_workload(other, torch, dev)

@@ -283,6 +283,34 @@ mx_status mx_grouped_mm_wgrad_hp(const void* g, const void* x,
                                  int64_t N, int64_t K, void* out,
                                  int32_t* dev_err, void* stream);
 
+/* FP8 (non-MX) with one power-of-two scale per row: the FP8 grouped-mm
+ * training variant ([P1], review thread: FP8GroupedMMConfig; [P2], Autograd
+ * func changes: FP8 MoE training, ~10% tokens/s on Llama4 Scout). The pages
+ * do not give its scaling; here each row of the quantized axis gets the
+ * scale the RCEIL rule picks for the whole row (nothing saturates), and a row
+ * with a NaN or infinity gets scale 0xFF and codes 0x7F with the element's
+ * sign. The byte is written once per 32-block in the MX_SCALES_K128 layout,
+ * so these are MX operands whose block scales along a row are equal: the
+ * MXFP8 GEMMs above compute the row-scaled FP8 GEMMs unchanged.
+ *
+ * Row-wise: x bf16 [batch, rows, cols] (row stride ld) -> q [batch, rows,
+ * cols], s [batch, cols/128, rows, 4]. cols % 128 == 0. */
+mx_status mx_quantize_fp8_rowwise(const void* x, int64_t batch, int64_t rows,
+                                  int64_t cols, int64_t ld, uint8_t* q,
+                                  uint8_t* s, void* stream);
+
+/* Column-wise: q [batch, cols, rows] with one scale per column, or, with
+ * offs (device int32 [E], exclusive ends along rows, multiples of 128, as
+ * the grouped GEMMs take them), one scale per (column, group) and one for
+ * the rows after offs[E-1] (the weight gradient contracts each group's tokens
+ * separately). s [batch, rows/128, cols, 4]. rows % 128 == 0,
+ * cols % 128 == 0. work: caller-owned device scratch of batch * (E + 1) *
+ * cols int32 (batch * cols without offs), overwritten. Three kernels. */
+mx_status mx_quantize_fp8_colwise(const void* x, int64_t batch, int64_t rows,
+                                  int64_t cols, int64_t ld,
+                                  const int32_t* offs, int32_t E, uint8_t* q,
+                                  uint8_t* s, int32_t* work, void* stream);
+
 /* Per-group token padding ([P1], the torchtitan commit adding
  * pad_token_groups_for_grouped_mm; [P3], The integration: pad_multiple=128).
  * x: [T, row_bytes] rows (any element type), tokens grouped by expert in

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxfp8.so")
-SOURCES = ["mx_quant.hip", "mx_gemm.hip", "mx_pad_hp.hip", "mx_abi.cpp"]
+SOURCES = ["mx_quant.hip", "mx_gemm.hip", "mx_pad_hp.hip", "mx_fp8.hip", "mx_abi.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from emitting packed float32 VALU ops.

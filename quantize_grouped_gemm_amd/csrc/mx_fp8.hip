@@ -1,0 +1,146 @@
+// FP8 E4M3 with one power-of-two scale per row, gfx950: the non-MX FP8
+// grouped-mm training variant. Its scaling is not on the pages that define
+// the method (they name FP8GroupedMMConfig and its ~10% tokens/s for FP8 MoE
+// training, and say its support was set aside in favour of MXFP8); here each
+// row of the quantized axis gets the scale the RCEIL rule picks for the whole
+// row, and the weight gradient's operands get one scale per (column, group).
+// The scale byte is written once per 32-block, in the k128 layout, so the
+// operands are MX operands whose block scales along a row are equal and the
+// MXFP8 GEMMs compute the row-scaled GEMM unchanged.
+//
+//   k_fp8_rowscale   16 whole rows per workgroup (16 lanes per row): a pass
+//                    for the row maximum, a second pass for the codes
+//   k_fp8_col_amax   per 128 x 128 tile, column maxima folded into the
+//                    caller's int32 workspace [batch, segments, cols] with
+//                    atomic max (segments: the groups of the row offsets,
+//                    plus the rows after the last)
+//   k_fp8_col_quant  per tile, column-wise codes with the column's scale
+//                    (the shared column tile routine with given scales)
+
+#include "mx_device.h"
+#include "mx_kernels.h"
+#include "mx_tile.h"
+
+#include <algorithm>
+
+namespace mxk {
+
+constexpr int kRowsPerGroup = 16;   // rows of one k_fp8_rowscale workgroup
+
+__global__ __launch_bounds__(256) void k_fp8_rowscale(Fp8Args a) {
+  const int t = threadIdx.x, cc = t & 15;
+  const int64_t b = blockIdx.y;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerGroup + (t >> 4);
+  const bool ok = row < a.rows;
+  const uint16_t* x = a.x + (b * a.rows + (ok ? row : 0)) * a.ld;
+  const int steps = (int)(a.cols / 128);
+  uint32_t m = 0;
+  if (ok)
+    for (int it = 0; it < steps; ++it)
+      m = max(m, absmax8_bits(*reinterpret_cast<const uint4*>(x + it * 128 + cc * 8)));
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d));
+  const uint32_t sb = scale_byte(m, true);
+  if (!ok) return;
+  uint8_t* q = a.q + (b * a.rows + row) * a.cols;
+  uint32_t* s = reinterpret_cast<uint32_t*>(a.s) + b * steps * a.rows;
+  for (int it = 0; it < steps; ++it) {
+    const uint4 v = *reinterpret_cast<const uint4*>(x + it * 128 + cc * 8);
+    *reinterpret_cast<uint2*>(q + it * 128 + cc * 8) = e4m3_chunk(v, sb, false);
+    if (cc == 0) s[it * a.rows + row] = sb * 0x01010101u;
+  }
+}
+
+// Segment of row r: the first group whose end lies past r (E for the rows
+// after the last end, or 0 without offsets).
+__device__ __forceinline__ int row_segment(const Fp8Args& a, int64_t r) {
+  if (!a.offs) return 0;
+  int lo = 0, hi = a.E;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)a.offs[mid] > r) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void k_fp8_clear(Fp8Args a) {
+  const int64_t n = a.batch * a.segments * a.cols;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    a.work[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void k_fp8_col_amax(Fp8Args a) {
+  __shared__ uint32_t part[4][kTC];
+  const int t = threadIdx.x, cc = t & 15, lane = t & 63, w = t >> 6;
+  const int64_t b = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.y * kTR, c0 = (int64_t)blockIdx.x * kTC;
+  uint4 v[kTileChunks];
+  const uint16_t* x = a.x + (b * a.rows + r0) * a.ld + c0;
+  // magnitudes of the thread's 8 columns, maximum over its 8 rows
+  uint32_t m[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < kTileChunks; ++j) {
+    v[j] = *reinterpret_cast<const uint4*>(x + ((t >> 4) + 16 * j) * a.ld + cc * 8);
+    const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      m[k] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(mx_us2, m[k]),
+                                                                    __builtin_bit_cast(mx_us2, w4[k] & 0x7FFF7FFFu)));
+  }
+  // the other rows of the wave with the same columns: lanes ^ 16, ^ 32
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+#pragma unroll
+    for (int d = 16; d < 64; d <<= 1)
+      m[k] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(mx_us2, m[k]),
+                                                                    __builtin_bit_cast(mx_us2, (uint32_t)__shfl_xor((int)m[k], d))));
+  }
+  if (lane < 16)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      part[w][cc * 8 + 2 * k] = m[k] & 0xFFFFu;
+      part[w][cc * 8 + 2 * k + 1] = m[k] >> 16;
+    }
+  __syncthreads();
+  if (t < kTC) {
+    const uint32_t mm = max(max(part[0][t], part[1][t]), max(part[2][t], part[3][t]));
+    const int seg = row_segment(a, r0);
+    atomicMax(reinterpret_cast<unsigned int*>(a.work) + (b * a.segments + seg) * a.cols + c0 + t, mm);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fp8_col_quant(Fp8Args a) {
+  __shared__ uint4 lds[kTR * kTC / 8];
+  __shared__ uint8_t sb[kTC];
+  const int t = threadIdx.x;
+  const int64_t b = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.y * kTR, c0 = (int64_t)blockIdx.x * kTC;
+  if (t < kTC) {
+    const int seg = row_segment(a, r0);
+    const uint32_t mm = reinterpret_cast<const uint32_t*>(a.work)[(b * a.segments + seg) * a.cols + c0 + t];
+    sb[t] = (uint8_t)scale_byte(mm, true);
+  }
+  uint4 v[kTileChunks];
+  tile_load(v, a.x + (b * a.rows + r0) * a.ld + c0, a.ld, kTR, kTC);
+  tile_to_lds(v, lds);
+  __syncthreads();
+  tile_colq(lds, kTR, kTC, true, TileOut{a.q + b * a.rows * a.cols, a.s + b * a.rows * (a.cols / kBlock), a.rows, a.cols, true},
+            r0, c0, sb);
+}
+
+hipError_t launch_fp8_rowscale(const Fp8Args& a, hipStream_t s) {
+  dim3 grid((unsigned)((a.rows + kRowsPerGroup - 1) / kRowsPerGroup), (unsigned)a.batch);
+  hipLaunchKernelGGL(k_fp8_rowscale, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_colscale(const Fp8Args& a, hipStream_t s) {
+  const int64_t n = a.batch * a.segments * a.cols;
+  hipLaunchKernelGGL(k_fp8_clear, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0, s, a);
+  dim3 grid((unsigned)(a.cols / kTC), (unsigned)(a.rows / kTR), (unsigned)a.batch);
+  hipLaunchKernelGGL(k_fp8_col_amax, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_fp8_col_quant, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mxk

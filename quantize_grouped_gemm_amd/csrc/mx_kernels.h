@@ -72,6 +72,19 @@ struct GemmArgs {
   bool rceil = true;
 };
 
+// FP8 row-scaled quantization (one scale per row; column-wise: per column
+// and segment of rows). Codes are row-major [batch, rows, cols] (row-wise)
+// or [batch, cols, rows] (column-wise); scales in the k128 layout.
+struct Fp8Args {
+  const uint16_t* x;
+  int64_t batch, rows, cols, ld;
+  uint8_t *q, *s;
+  const int32_t* offs;   // column-wise: segment ends along rows (nullable)
+  int32_t E;
+  int64_t segments;      // column-wise: E + 1 with offsets, else 1
+  int32_t* work;         // column-wise: [batch, segments, cols] int32 maxima
+};
+
 struct PadArgs {
   const uint8_t* x;
   const int32_t* sizes;
@@ -104,6 +117,8 @@ hipError_t launch_gemm_wgrad(const GemmArgs& a, hipStream_t s);
 // lda / ldb their row pitches in bytes, out bf16 [E, N, K].
 hipError_t launch_gemm_wgrad_hp(const GemmArgs& a, hipStream_t s);
 hipError_t launch_pad(const PadArgs& a, hipStream_t s);
+hipError_t launch_fp8_rowscale(const Fp8Args& a, hipStream_t s);
+hipError_t launch_fp8_colscale(const Fp8Args& a, hipStream_t s);
 hipError_t launch_pad_map(const PadArgs& a, hipStream_t s);   // offs_pad and src_row only
 hipError_t launch_unpad(const UnpadArgs& a, hipStream_t s);
 

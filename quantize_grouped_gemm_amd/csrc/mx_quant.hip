@@ -27,21 +27,6 @@
 
 namespace mxk {
 
-// Loads the thread's chunks of a bf16 tile whose (0,0) is `base` with row
-// stride ld elements; chunks outside the valid region read as zero.
-__device__ __forceinline__ void tile_load(uint4 (&v)[kTileChunks], const uint16_t* base,
-                                          int64_t ld, int rows_valid, int cols_valid) {
-  const int t = threadIdx.x;
-  const int cc = t & 15;
-#pragma unroll
-  for (int j = 0; j < kTileChunks; ++j) {
-    const int row = (t >> 4) + 16 * j;
-    v[j] = (row < rows_valid && cc * 8 < cols_valid)
-               ? *reinterpret_cast<const uint4*>(base + row * ld + cc * 8)
-               : make_uint4(0, 0, 0, 0);
-  }
-}
-
 // tile_load through a row map: tile row `row` reads input row
 // src_row[r0 + row], or zeros where that is negative or past src_rows.
 __device__ __forceinline__ void tile_load_gather(uint4 (&v)[kTileChunks], const uint16_t* x, int64_t ld,

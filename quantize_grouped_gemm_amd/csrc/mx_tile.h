@@ -58,6 +58,21 @@ __device__ __forceinline__ void tile_rowq(const uint4 (&v)[kTileChunks], int row
   }
 }
 
+// Loads the thread's chunks of a bf16 tile whose (0,0) is `base` with row
+// stride ld elements; chunks outside the valid region read as zero.
+__device__ __forceinline__ void tile_load(uint4 (&v)[kTileChunks], const uint16_t* base,
+                                          int64_t ld, int rows_valid, int cols_valid) {
+  const int t = threadIdx.x;
+  const int cc = t & 15;
+#pragma unroll
+  for (int j = 0; j < kTileChunks; ++j) {
+    const int row = (t >> 4) + 16 * j;
+    v[j] = (row < rows_valid && cc * 8 < cols_valid)
+               ? *reinterpret_cast<const uint4*>(base + row * ld + cc * 8)
+               : make_uint4(0, 0, 0, 0);
+  }
+}
+
 // Stage the thread's chunks in LDS: tile row r, 16-byte unit u (columns
 // 8 u .. 8 u + 7) at slot r * 16 + (u ^ g(r)), g(r) = 2 ((r >> 4) & 7). A
 // ds_write_b128 pass (16 lanes = one row) covers the 64 banks once.
@@ -77,9 +92,12 @@ __device__ __forceinline__ void tile_to_lds(const uint4 (&v)[kTileChunks], uint4
 // maxima pair lanes q, q ^ 1 (one DPP exchange). The LDS reads (one dword =
 // two columns, 16 rows) hit 64 distinct banks thanks to the swizzle above.
 // Output row = tile column c0 + col, output column = tile row r0 + row.
+// col_sb (optional, 128 bytes by tile column): scale bytes given per column
+// (one scale for the whole column) in place of the blocks' own.
 // All lanes must reach this function.
 __device__ __forceinline__ void tile_colq(const uint4* lds4, int rows_valid, int cols_valid,
-                                          bool rceil, TileOut o, int64_t r0, int64_t c0) {
+                                          bool rceil, TileOut o, int64_t r0, int64_t c0,
+                                          const uint8_t* col_sb = nullptr) {
   const uint32_t* lds = reinterpret_cast<const uint32_t*>(lds4);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane & 7;
@@ -95,8 +113,8 @@ __device__ __forceinline__ void tile_colq(const uint4* lds4, int rows_valid, int
     uint32_t mm = __builtin_bit_cast(uint32_t, m);
     const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)mm, 0xB1, 0xF, 0xF, false);   // lane ^ 1
     m = __builtin_elementwise_max(m, __builtin_bit_cast(mx_us2, other));
-    const uint32_t sb0 = scale_byte(m.x, rceil);
-    const uint32_t sb1 = scale_byte(m.y, rceil);
+    const uint32_t sb0 = col_sb ? (uint32_t)col_sb[2 * cp] : scale_byte(m.x, rceil);
+    const uint32_t sb1 = col_sb ? (uint32_t)col_sb[2 * cp + 1] : scale_byte(m.y, rceil);
     if (!rceil) {
       const uint32_t lim2 = sat_bits(sb0) | (sat_bits(sb1) << 16);
 #pragma unroll

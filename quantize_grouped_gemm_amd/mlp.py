@@ -49,7 +49,7 @@ def _qbytes(n, dual):
     return n * (2 + (2 if dual else 1) * (1 + 1 / 32))
 
 
-_WEIGHT_STAGES = ("quant_w13", "quant_w2")
+_WEIGHT_STAGES = ("quant_w13", "quant_w2", "fp8_w13", "fp8_w2")
 
 
 def _weights_cached(stages, quantize_weights):
@@ -157,25 +157,32 @@ class MoEMLP:
     `multiple` rows inside a capacity of Tcap rows."""
 
     def __init__(self, E, T, D, H, Tcap, device, mode="rceil", wgrad="mx", wgrad_dtype=torch.float32,
-                 multiple=128):
+                 multiple=128, recipe="mxfp8"):
         self.E, self.T, self.D, self.H, self.Tcap = E, T, D, H, Tcap
-        self.mode, self.wgrad, self.multiple = mode, wgrad, multiple
+        self.mode, self.wgrad, self.multiple, self.recipe = mode, wgrad, multiple, recipe
         dev = device
         bf = torch.bfloat16
-        mxw = wgrad == "mx"
+        fp8 = recipe == "fp8_rowwise"
+        if fp8:
+            wgrad = self.wgrad = "mx"   # the FP8 weight gradients run on FP8 operands
+        mxw = wgrad == "mx" and not fp8
         # bf16 padded copies exist only for the hp weight gradient; the MXFP8
         # recipe pads while it quantizes
         self.x_pad = None if mxw else torch.empty((Tcap, D), dtype=bf, device=dev)
         self.dy_pad = None if mxw else torch.empty((Tcap, D), dtype=bf, device=dev)
+        if fp8:
+            # FP8 row-scaled operands of h and dA|dB, quantized from their bf16 values
+            self.qh8 = _q_out((), Tcap, H, dev)
+            self.qdz8 = _q_out((), Tcap, 2 * H, dev)
         self.offs = torch.empty((E,), dtype=torch.int32, device=dev)
         self.src = torch.empty((Tcap,), dtype=torch.int32, device=dev)
         self.offs2 = torch.empty((E,), dtype=torch.int32, device=dev)
         self.src2 = torch.empty((Tcap,), dtype=torch.int32, device=dev)
         self.err = torch.zeros((1,), dtype=torch.int32, device=dev)
-        self.qx = _q_out((), Tcap, D, dev, True, mxw)
+        self.qx = _q_out((), Tcap, D, dev, True, mxw or fp8)
         self.q13 = _q_out((E,), 2 * H, D, dev)
         self.q2 = _q_out((E,), D, H, dev)
-        self.qdy = _q_out((), Tcap, D, dev, True, mxw)
+        self.qdy = _q_out((), Tcap, D, dev, True, mxw or fp8)
         self.z = torch.empty((Tcap, 2 * H), dtype=bf, device=dev)
         self.hq = _q_out((), Tcap, H, dev)
         if not mxw:
@@ -186,7 +193,7 @@ class MoEMLP:
         if not mxw:
             self.dzq["dab"] = torch.empty((Tcap, 2 * H), dtype=bf, device=dev)
         self.dx = torch.empty((T, D), dtype=bf, device=dev)
-        wdt = wgrad_dtype if mxw else bf
+        wdt = wgrad_dtype if mxw or fp8 else bf
         self.dw2 = torch.empty((E, D, H), dtype=wdt, device=dev)
         self.dw13 = torch.empty((E, 2 * H, D), dtype=wdt, device=dev)
 
@@ -205,6 +212,8 @@ class MoEMLP:
         return _weights_cached(self._stages(x, sizes, w13, w2, dy), quantize_weights)
 
     def _stages(self, x, sizes, w13, w2, dy):
+        if self.recipe == "fp8_rowwise":
+            return self._stages_fp8(x, sizes, w13, w2, dy)
         E, T, D, H, Tc, m = self.E, self.T, self.D, self.H, self.Tcap, self.mode
         mxw = self.wgrad == "mx"
         z0, z1 = self.z[:, :H], self.z[:, H:]
@@ -281,6 +290,61 @@ class MoEMLP:
                             lambda: mx.grouped_mm_wgrad_hp(self.dzq["dab"], self.x_pad, self.offs,
                                                            out=self.dw13, dev_err=err)))
         return st
+
+    def _stages_fp8(self, x, sizes, w13, w2, dy):
+        """The step with FP8 row-scaled operands (one power-of-two scale per
+        row; the weight-gradient operands per column and group): the same
+        grouped GEMMs, with the quantizations done by the FP8 kernels from
+        bf16 tensors (h and dA|dB kept in bf16 for them)."""
+        E, T, D, H, Tc, m = self.E, self.T, self.D, self.H, self.Tcap, self.mode
+        z0, z1 = self.z[:, :H], self.z[:, H:]
+        err = self.err
+        fq = mx.quantize_fp8
+        return [
+            Stage("pad_x", "k_pad", 0, 2 * T * D + 2 * Tc * D,
+                  lambda: mx.pad_groups(x, sizes, Tc, self.multiple,
+                                        out=dict(x_pad=self.x_pad, offs=self.offs, src_row=self.src),
+                                        dev_err=err)),
+            Stage("fp8_x", "k_fp8", 0, _qbytes(Tc * D, True) + 2 * Tc * D,
+                  lambda: fq(self.x_pad, True, True, offs=self.offs, out=self.qx)),
+            Stage("fp8_w13", "k_fp8", 0, _qbytes(E * 2 * H * D, True) + 2 * E * 2 * H * D,
+                  lambda: fq(w13, True, True, out=self.q13)),
+            Stage("fp8_w2", "k_fp8", 0, _qbytes(E * D * H, True) + 2 * E * D * H,
+                  lambda: fq(w2, True, True, out=self.q2)),
+            Stage("gemm_w13_fwd", "k_gemm_grouped", 2 * T * 2 * H * D, 0,
+                  lambda: mx.grouped_mm_fwd(self.qx["q_row"], self.qx["s_row"], self.q13["q_row"],
+                                            self.q13["s_row"], self.offs, out=self.z, dev_err=err)),
+            Stage("swiglu_fwd", "k_swiglu_fwd", 0, Tc * H * (4 + 2 * (1 + 1 / 32) + 2),
+                  lambda: mx.swiglu_quant_fwd(z0, z1, m, want_h=True, out=self.hq)),
+            Stage("fp8_h", "k_fp8", 0, _qbytes(Tc * H, True) + 2 * Tc * H,
+                  lambda: fq(self.hq["h"], True, True, offs=self.offs, out=self.qh8)),
+            Stage("gemm_w2_fwd", "k_gemm_grouped", 2 * T * D * H, 0,
+                  lambda: mx.grouped_mm_fwd_unpad(self.qh8["q_row"], self.qh8["s_row"], self.q2["q_row"],
+                                                  self.q2["s_row"], self.offs, sizes, T, out=self.y, dev_err=err)),
+            Stage("pad_dy", "k_pad", 0, 2 * T * D + 2 * Tc * D,
+                  lambda: mx.pad_groups(dy, sizes, Tc, self.multiple,
+                                        out=dict(x_pad=self.dy_pad, offs=self.offs2, src_row=self.src2),
+                                        dev_err=err)),
+            Stage("fp8_dy", "k_fp8", 0, _qbytes(Tc * D, True) + 2 * Tc * D,
+                  lambda: fq(self.dy_pad, True, True, offs=self.offs, out=self.qdy)),
+            Stage("gemm_w2_dgrad", "k_gemm_grouped", 2 * T * D * H, 0,
+                  lambda: mx.grouped_mm_dgrad(self.qdy["q_row"], self.qdy["s_row"], self.q2["q_col"],
+                                              self.q2["s_col"], self.offs, out=self.dh, dev_err=err)),
+            Stage("gemm_w2_wgrad", "k_gemm_wgrad", 2 * T * D * H, 0,
+                  lambda: mx.grouped_mm_wgrad(self.qdy["q_col"], self.qdy["s_col"], self.qh8["q_col"],
+                                              self.qh8["s_col"], self.offs, out=self.dw2, dev_err=err)),
+            Stage("swiglu_bwd", "k_swiglu_bwd", 0, Tc * H * (6 + 4 * (1 + 1 / 32) + 4),
+                  lambda: mx.swiglu_quant_bwd(self.dh, z0, z1, m, want_dab=True, out=self.dzq)),
+            Stage("fp8_dz", "k_fp8", 0, _qbytes(Tc * 2 * H, True) + 2 * Tc * 2 * H,
+                  lambda: fq(self.dzq["dab"], True, True, offs=self.offs, out=self.qdz8)),
+            Stage("gemm_w13_dgrad", "k_gemm_grouped", 2 * T * 2 * H * D, 0,
+                  lambda: mx.grouped_mm_dgrad_unpad(self.qdz8["q_row"], self.qdz8["s_row"], self.q13["q_col"],
+                                                    self.q13["s_col"], self.offs, sizes, T, out=self.dx,
+                                                    dev_err=err)),
+            Stage("gemm_w13_wgrad", "k_gemm_wgrad", 2 * T * 2 * H * D, 0,
+                  lambda: mx.grouped_mm_wgrad(self.qdz8["q_col"], self.qdz8["s_col"], self.qx["q_col"],
+                                              self.qx["s_col"], self.offs, out=self.dw13, dev_err=err)),
+        ]
 
     def gemm_flops(self):
         """Useful GEMM flops of one step (real tokens only)."""

@@ -30,7 +30,7 @@ def _declared():
 def test_header_symbols_exported_and_bound():
     L = _lib()
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), n
     assert sorted(mx.EXPORTS) == names
@@ -64,6 +64,11 @@ def test_argument_errors_are_reported_without_device_work():
     assert L.mx_scaled_grouped_mm_wgrad(p, p, p, p, p, 0, 128, 64, 64, 1, p, None, None) == 2
     assert L.mx_pad_groups(p, p, 2, 10, 24, 128, 256, p, p, p, None, None) == 2
     assert L.mx_unpad_groups(p, p, 128, 10, 32, None, None) == 1
+    # FP8 row-scaled: cols not a multiple of 128; column-wise rows not a
+    # multiple of 128; offsets without a group count
+    assert L.mx_quantize_fp8_rowwise(p, 1, 64, 96, 96, p, p, None) == 2
+    assert L.mx_quantize_fp8_colwise(p, 1, 96, 128, 128, None, 0, p, p, p, None) == 2
+    assert L.mx_quantize_fp8_colwise(p, 1, 128, 128, 128, p, 0, p, p, p, None) == 2
     # fused w13 + SwiGLU: H not a multiple of 128, bad mode
     assert L.mx_scaled_grouped_mm_swiglu_fwd(p, p, p, p, p, 4, 256, 96, 128, 0, p, p, p, p, p, None, None,
                                              None) == 2

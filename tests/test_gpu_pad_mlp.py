@@ -138,6 +138,29 @@ def test_moe_mlp_step_matches_oracle(gpu, wgrad):
         assert _sqnr(rdw13[g], dw13[g]) > 35
 
 
+def test_moe_mlp_step_fp8_rowwise_matches_oracle(gpu):
+    """The FP8 row-scaled recipe of the routed-experts step against the
+    oracle's same composition (quantize_fp8_bf16 throughout)."""
+    E, T, D, H = 4, 600, 256, 128
+    sizes = np.array([250, 0, 300, 50], np.int32)
+    Tcap = synth.capacity(T, E)
+    x, w1, w3, w2, dy = synth.mlp_inputs(T, D, H, E=E, seed=6)
+    net = mlp.MoEMLP(E, T, D, H, Tcap, dev(), recipe="fp8_rowwise")
+    w13 = torch.cat([w1, w3], dim=1).to(dev())
+    net.step(x.to(dev()), to_dev(sizes), w13, w2.to(dev()), dy.to(dev()))
+    ref = O.moe_mlp_step(synth.bits(x), sizes, *[synth.bits(t) for t in (w1, w3, w2, dy)], "rceil", Tcap,
+                         recipe="fp8_rowwise")
+    torch.cuda.synchronize()
+    assert int(net.err.item()) == 0
+    for k, got in (("y", net.y), ("dx", net.dx)):
+        assert _sqnr(O.bf16_to_f64(ref[k]), O.bf16_to_f64(bf16_host(got))) > 35, k
+    dw2, dw13 = host(net.dw2), host(net.dw13)
+    assert np.all(dw2[1] == 0) and np.all(dw13[1] == 0)
+    for g in (0, 2, 3):
+        assert _sqnr(ref["dw2"][g], dw2[g]) > 35
+        assert _sqnr(ref["dw13"][g], dw13[g]) > 35
+
+
 def test_moe_step_with_cached_weight_quantization(gpu):
     """Micro-batches of one optimizer step share one dual quantization of
     the expert weights: a step that reuses the cached MXFP8 weights gives the
