@@ -531,7 +531,7 @@ def dense_mlp_step(x, w1, w3, w2, dy, mode, wgrad_dtype="f32"):
 
 
 def moe_mlp_step(x, sizes, w1, w3, w2, dy, mode, Tcap, multiple=128,
-                 wgrad="mx", wgrad_dtype="f32"):
+                 wgrad="mx", wgrad_dtype="f32", recipe="mxfp8"):
     """One routed-experts grouped MLP forward + backward in MXFP8.
 
     x, dy [T, D] bf16 bits in expert-major order; sizes [E] tokens per
@@ -539,7 +539,12 @@ def moe_mlp_step(x, sizes, w1, w3, w2, dy, mode, Tcap, multiple=128,
     rows (pad_groups), run through the grouped GEMMs and unpadded.
     wgrad = "mx" (MXFP8 weight gradients, float ``wgrad_dtype``) or "hp"
     (wgrad_with_hp: bf16 operands, bf16 result).
+    recipe = "fp8_rowwise": every operand is quantized with one scale per
+    row instead (quantize_fp8_bf16; the weight-gradient operands per column
+    and group), h and dA|dB from their bf16 values.
     """
+    if recipe == "fp8_rowwise":
+        return _moe_mlp_step_fp8(x, sizes, w1, w3, w2, dy, Tcap, multiple, wgrad_dtype)
     T = x.shape[0]
     H = w1.shape[1]
     w13 = np.concatenate([w1, w3], axis=1)          # [E, 2H, D]
@@ -563,4 +568,29 @@ def moe_mlp_step(x, sizes, w1, w3, w2, dy, mode, Tcap, multiple=128,
         dw13 = f64_to_bf16(grouped_mm_wgrad_hp(bw["dab"], x_pad, offs))
     return dict(offs=offs, src_row=src, x_pad=x_pad, z=z, h=sw["h"],
                 y=unpad_groups(y_pad, src, T), dh=dh, dab=bw["dab"],
+                dx=unpad_groups(dx_pad, src, T), dw2=dw2, dw13=dw13)
+
+
+def _moe_mlp_step_fp8(x, sizes, w1, w3, w2, dy, Tcap, multiple, wgrad_dtype):
+    """moe_mlp_step with FP8 row-scaled operands (see quantize_fp8_bf16)."""
+    T = x.shape[0]
+    H = w1.shape[1]
+    w13 = np.concatenate([w1, w3], axis=1)          # [E, 2H, D]
+    x_pad, offs, src = pad_groups(x, sizes, multiple, Tcap)
+    dy_pad, _, _ = pad_groups(dy, sizes, multiple, Tcap)
+    qx = quantize_fp8_bf16(x_pad, True, True, segments=offs)
+    q13 = quantize_fp8_bf16(w13, True, True)
+    q2 = quantize_fp8_bf16(w2, True, True)
+    z = f64_to_bf16(grouped_mm(qx["q_row"], qx["s_row"], q13["q_row"], q13["s_row"], offs))
+    h = swiglu_fwd(z[:, :H], z[:, H:])
+    qh = quantize_fp8_bf16(h, True, True, segments=offs)
+    y_pad = f64_to_bf16(grouped_mm(qh["q_row"], qh["s_row"], q2["q_row"], q2["s_row"], offs))
+    qdy = quantize_fp8_bf16(dy_pad, True, True, segments=offs)
+    dh = f64_to_bf16(grouped_mm(qdy["q_row"], qdy["s_row"], q2["q_col"], q2["s_col"], offs))
+    dab = swiglu_bwd(dh, z[:, :H], z[:, H:])
+    qdz = quantize_fp8_bf16(dab, True, True, segments=offs)
+    dx_pad = f64_to_bf16(grouped_mm(qdz["q_row"], qdz["s_row"], q13["q_col"], q13["s_col"], offs))
+    dw2 = _rt(grouped_mm_wgrad(qdy["q_col"], qdy["s_col"], qh["q_col"], qh["s_col"], offs), wgrad_dtype)
+    dw13 = _rt(grouped_mm_wgrad(qdz["q_col"], qdz["s_col"], qx["q_col"], qx["s_col"], offs), wgrad_dtype)
+    return dict(offs=offs, src_row=src, x_pad=x_pad, z=z, h=h, y=unpad_groups(y_pad, src, T), dh=dh, dab=dab,
                 dx=unpad_groups(dx_pad, src, T), dw2=dw2, dw13=dw13)
