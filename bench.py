@@ -33,7 +33,7 @@ PEAK_MXFP8 = 5.0e15      # MI355X dense MXFP8 / FP8 MFMA, FLOP/s
 PEAK_BF16 = 2.5e15       # dense BF16 MFMA
 PEAK_HBM = 8.0e12        # HBM3E bytes/s
 
-WORKLOADS = ("moe_scout", "moe_dsv3", "moe_dsv3_hp", "dense", "quant", "linear", "copy")
+WORKLOADS = ("moe_scout", "moe_dsv3", "moe_dsv3_hp", "dense", "quant", "linear", "copy", "vendor_gemm")
 
 # HBM traffic of the dominant kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # passes scaled by a 1 GiB copy (see the file); used only while the kernel's
@@ -273,6 +273,67 @@ def _fused_swiglu_component(torch, dev, reps=5):
             "unfused_total_us": round(gemm + swi, 1)}
 
 
+def _vendor_gemm_component(torch, dev, reps=10):
+    """The dense MXFP8 GEMM beside the vendor library on the same FP8 codes:
+    hipBLASLt through torch._scaled_mm with block-32 E8M0 scales, its
+    per-tensor-scaled FP8 GEMM and the bf16 matmul. Every scale is 2^0, so
+    all four compute the same product; the largest relative difference to
+    this library's output is reported."""
+    from quantize_grouped_gemm_amd import mx
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+
+    def codes(r, c):
+        mag = torch.randint(0, 0x7E, (r, c), generator=g, device=dev, dtype=torch.int32)
+        sign = torch.randint(0, 2, (r, c), generator=g, device=dev, dtype=torch.int32) * 0x80
+        return (mag | sign).to(torch.uint8)
+
+    def timed(f):
+        f()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                f()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / reps / 1e3)
+        return sorted(ts)[1]
+
+    res = {}
+    # the dense MLP's w13 and w2 forward shapes, a square one and a MoE-sized one
+    for M, N, K in ((8192, 28672, 4096), (8192, 4096, 14336), (8192, 8192, 8192), (16384, 16384, 5120)):
+        qa, qb = codes(M, K), codes(N, K)
+        sa = torch.full((K // 128, M, 4), 127, dtype=torch.uint8, device=dev)
+        sb = torch.full((K // 128, N, 4), 127, dtype=torch.uint8, device=dev)
+        out = mx.scaled_mm(qa, sa, qb, sb)
+        fl = 2.0 * M * N * K
+        r = {"this_mxfp8_tflops": round(fl / timed(lambda: mx.scaled_mm(qa, sa, qb, sb, out=out)) / 1e12, 1)}
+        A, B = qa.view(torch.float8_e4m3fn), qb.view(torch.float8_e4m3fn)
+        try:
+            ea = torch.full((M, K // 32), 127, dtype=torch.uint8, device=dev).view(torch.float8_e8m0fnu)
+            eb = torch.full((N, K // 32), 127, dtype=torch.uint8, device=dev).view(torch.float8_e8m0fnu)
+            ref = torch._scaled_mm(A, B.t(), scale_a=ea, scale_b=eb, out_dtype=torch.bfloat16)
+            r["hipblaslt_mxfp8_tflops"] = round(fl / timed(
+                lambda: torch._scaled_mm(A, B.t(), scale_a=ea, scale_b=eb, out_dtype=torch.bfloat16)) / 1e12, 1)
+            r["max_rel_diff_vs_hipblaslt_mxfp8"] = float(
+                ((out.float() - ref.float()).abs().max() / ref.float().abs().max()).item())
+            del ea, eb, ref
+        except Exception as e:   # MX scales not supported by this torch / library build
+            r["hipblaslt_mxfp8_tflops"] = f"unavailable: {type(e).__name__}"
+        one = torch.ones((), device=dev)
+        r["hipblaslt_fp8_tensorwise_tflops"] = round(fl / timed(
+            lambda: torch._scaled_mm(A, B.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)) / 1e12, 1)
+        Ab, Bb = A.to(torch.bfloat16), B.to(torch.bfloat16)
+        r["torch_bf16_matmul_tflops"] = round(fl / timed(lambda: Ab @ Bb.t()) / 1e12, 1)
+        res[f"{M}x{N}x{K}"] = r
+        del qa, qb, sa, sb, out, A, B, Ab, Bb
+        torch.cuda.empty_cache()
+    return res
+
+
 def _cpu_baseline():
     """The oracle on a bounded slice of the default workload: one expert with
     1024 of its 8192 hidden units and 128 tokens. Weight quantization and the
@@ -331,8 +392,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"workload": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30}))
         return
-    if name in ("quant", "linear"):
-        comp = _quant_component(torch, dev) if name == "quant" else _linear_component(torch, dev)
+    if name in ("quant", "linear", "vendor_gemm"):
+        comp = {"quant": _quant_component, "linear": _linear_component,
+                "vendor_gemm": _vendor_gemm_component}[name](torch, dev)
         print(json.dumps({"workload": name, **comp}))
         return
 

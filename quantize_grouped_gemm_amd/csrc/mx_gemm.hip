@@ -433,8 +433,8 @@ struct Regs {
   uint32_t nsa[4], nsb[4];          // scales of the next step
 };
 
-// Interleaving hints: within the next scheduling region, alternate one MFMA
-// with `ds` LDS reads and `vm` vector-memory instructions.
+// Interleaving hints: within the next scheduling region, follow each of the
+// 16 MFMAs with `ds` LDS reads and `vm` vector-memory instructions.
 template <int DS, int VM>
 __device__ __forceinline__ void interleave() {
 #pragma unroll
@@ -455,7 +455,10 @@ __device__ __forceinline__ void interleave() {
 //   3. the DMA of step ks+2 into `cur` (the last step, once past the end:
 //      it is never read) and the L2 prefetch of step ks+4 are issued while
 //      sub-step 1's MFMAs run and step ks+1's sub-step 0 operands and scales
-//      are read from `nxt`.
+//      are read from `nxt`. The DMA goes out one instruction per MFMA: the
+//      CU's texture path takes about 16 clocks per 1 KB instruction, so
+//      issued in a burst the four waves' DMA fills its queue and the
+//      next MFMA waits behind a stalled load.
 // The MFMA unit thus sees no gap for LDS latency or DMA issue; only the
 // barrier itself lies between the two halves. The last step runs the same
 // code: its DMA rewrites a free buffer and its reads of `nxt` go unused,
@@ -475,7 +478,7 @@ __device__ __forceinline__ void step_full(const TileDma& d, int ks, int nk, uint
   mfmas<1>(r.a1, r.b1, r.sva, r.svb, 8 * (lane >> 5), acc);
   load_ops<0>(nxt, r.a0, r.b0, wm, wn, lane);
   load_scales(nxt, r.nsa, r.nsb, wm, wn, lane);
-  interleave<2, 2>();
+  interleave<2, 1>();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
