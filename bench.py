@@ -33,7 +33,8 @@ PEAK_MXFP8 = 5.0e15      # MI355X dense MXFP8 / FP8 MFMA, FLOP/s
 PEAK_BF16 = 2.5e15       # dense BF16 MFMA
 PEAK_HBM = 8.0e12        # HBM3E bytes/s
 
-WORKLOADS = ("moe_scout", "moe_dsv3", "moe_dsv3_hp", "dense", "quant", "linear", "copy", "vendor_gemm")
+WORKLOADS = ("moe_scout", "moe_scout_fp8", "moe_dsv3", "moe_dsv3_hp", "dense", "quant", "linear", "copy",
+             "vendor_gemm")
 
 # HBM traffic of the dominant kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # passes scaled by a 1 GiB copy (see the file); used only while the kernel's
@@ -418,7 +419,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8",
+        "dtype": "fp8e4m3, one power-of-two scale per row" if name == "moe_scout_fp8" else "mxfp8",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, routed group sizes)",
         "config": config,
         "roofline": _roofline_gemm(table, gemm_kernel, PEAK_MXFP8,

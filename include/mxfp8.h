@@ -311,6 +311,21 @@ mx_status mx_quantize_fp8_colwise(const void* x, int64_t batch, int64_t rows,
                                   const int32_t* offs, int32_t E, uint8_t* q,
                                   uint8_t* s, int32_t* work, void* stream);
 
+/* Both directions of the same tensor at once: the codes and scales that
+ * mx_quantize_fp8_rowwise and mx_quantize_fp8_colwise (with the same offs)
+ * write, bit for bit, from two reads of x instead of four. One pass folds
+ * row and column maxima into work; a second quantizes each 128 x 128 tile
+ * both ways. q_row [batch, rows, cols], s_row [batch, cols/128, rows, 4];
+ * q_col [batch, cols, rows], s_col [batch, rows/128, cols, 4].
+ * rows % 128 == 0, cols % 128 == 0. work: caller-owned device scratch of
+ * batch * ((E + 1) * cols + rows) int32 (batch * (cols + rows) without
+ * offs), overwritten. Three kernels. */
+mx_status mx_quantize_fp8_dual(const void* x, int64_t batch, int64_t rows,
+                               int64_t cols, int64_t ld, const int32_t* offs,
+                               int32_t E, uint8_t* q_row, uint8_t* s_row,
+                               uint8_t* q_col, uint8_t* s_col, int32_t* work,
+                               void* stream);
+
 /* Per-group token padding ([P1], the torchtitan commit adding
  * pad_token_groups_for_grouped_mm; [P3], The integration: pad_multiple=128).
  * x: [T, row_bytes] rows (any element type), tokens grouped by expert in

@@ -470,6 +470,30 @@ mx_status mx_quantize_fp8_colwise(const void* x, int64_t batch, int64_t rows, in
   return launched(mxk::launch_fp8_colscale(a, as_stream(stream)), fn);
 }
 
+mx_status mx_quantize_fp8_dual(const void* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
+                               const int32_t* offs, int32_t E, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                               uint8_t* s_col, int32_t* work, void* stream) {
+  const char* fn = "mx_quantize_fp8_dual";
+  MX_REQUIRE(batch >= 0 && rows >= 0 && cols >= 0, MX_ERR_SHAPE, "%s: negative size", fn);
+  MX_REQUIRE(rows % 128 == 0 && cols % 128 == 0, MX_ERR_SHAPE, "%s: rows and cols must be multiples of 128", fn);
+  MX_REQUIRE(ld >= cols && ld % 8 == 0, MX_ERR_ALIGN, "%s: ld must be >= cols and a multiple of 8", fn);
+  MX_REQUIRE(!offs || (E >= 1 && E <= 1024), MX_ERR_SHAPE, "%s: E must be in [1, 1024] with offsets", fn);
+  MX_REQUIRE(rows / 128 <= 65535 && cols / 128 <= 0x7FFFFFFF && batch <= 65535, MX_ERR_SHAPE,
+             "%s: too large for one launch", fn);
+  if (batch == 0 || rows == 0 || cols == 0) return MX_OK;
+  MX_REQUIRE(x && q_row && s_row && q_col && s_col && work, MX_ERR_NULL, "%s: NULL pointer", fn);
+  MX_REQUIRE(al16(x) && al16(q_row) && al16(q_col) && al4(s_row) && al4(s_col) && al4(work), MX_ERR_ALIGN,
+             "%s: misaligned pointer", fn);
+  MX_DEVICE();
+  const int64_t segments = offs ? (int64_t)E + 1 : 1;
+  mxk::Fp8Args a{static_cast<const uint16_t*>(x), batch, rows, cols, ld, q_row, s_row, offs, offs ? E : 0,
+                 segments, work};
+  a.q_col = q_col;
+  a.s_col = s_col;
+  a.row_max = work + batch * segments * cols;
+  return launched(mxk::launch_fp8_dual(a, as_stream(stream)), fn);
+}
+
 mx_status mx_unpad_groups(const void* y_pad, const int32_t* src_row, int64_t Tcap, int64_t T, int64_t row_bytes,
                           void* y, void* stream) {
   const char* fn = "mx_unpad_groups";

@@ -16,6 +16,10 @@
 //                    plus the rows after the last)
 //   k_fp8_col_quant  per tile, column-wise codes with the column's scale
 //                    (the shared column tile routine with given scales)
+//   k_fp8_amax_rc    both directions at once: per tile, row maxima and
+//                    column maxima folded into the workspace (one read)
+//   k_fp8_dual_quant per tile, row-wise and column-wise codes from one read
+//                    with the scales the maxima give
 
 #include "mx_device.h"
 #include "mx_kernels.h"
@@ -63,24 +67,24 @@ __device__ __forceinline__ int row_segment(const Fp8Args& a, int64_t r) {
   return lo;
 }
 
+// Zeroes the column maxima, and the row maxima that follow them when
+// both directions are asked for.
 __global__ __launch_bounds__(256) void k_fp8_clear(Fp8Args a) {
-  const int64_t n = a.batch * a.segments * a.cols;
+  const int64_t n = a.batch * a.segments * a.cols + (a.row_max ? a.batch * a.rows : 0);
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     a.work[i] = 0;
 }
 
-__global__ __launch_bounds__(256) void k_fp8_col_amax(Fp8Args a) {
-  __shared__ uint32_t part[4][kTC];
+// Column maxima of the tile held in v (tile_load layout, (0,0) at row r0,
+// column c0 of batch entry b), folded into the column workspace with atomic
+// max. part: 4 x kTC dwords of LDS. All threads must reach this function.
+__device__ __forceinline__ void fold_col_max(const uint4 (&v)[kTileChunks], uint32_t (*part)[kTC], const Fp8Args& a,
+                                             int64_t b, int64_t r0, int64_t c0) {
   const int t = threadIdx.x, cc = t & 15, lane = t & 63, w = t >> 6;
-  const int64_t b = blockIdx.z;
-  const int64_t r0 = (int64_t)blockIdx.y * kTR, c0 = (int64_t)blockIdx.x * kTC;
-  uint4 v[kTileChunks];
-  const uint16_t* x = a.x + (b * a.rows + r0) * a.ld + c0;
   // magnitudes of the thread's 8 columns, maximum over its 8 rows
   uint32_t m[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < kTileChunks; ++j) {
-    v[j] = *reinterpret_cast<const uint4*>(x + ((t >> 4) + 16 * j) * a.ld + cc * 8);
     const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -109,6 +113,36 @@ __global__ __launch_bounds__(256) void k_fp8_col_amax(Fp8Args a) {
   }
 }
 
+__global__ __launch_bounds__(256) void k_fp8_col_amax(Fp8Args a) {
+  __shared__ uint32_t part[4][kTC];
+  const int64_t b = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.y * kTR, c0 = (int64_t)blockIdx.x * kTC;
+  uint4 v[kTileChunks];
+  tile_load(v, a.x + (b * a.rows + r0) * a.ld + c0, a.ld, kTR, kTC);
+  fold_col_max(v, part, a, b, r0, c0);
+}
+
+// Both directions: the row maxima of the tile (the 16 lanes of a row reduce
+// their chunks, as k_fp8_rowscale does over a whole row) and its column
+// maxima, each folded into its workspace with atomic max.
+__global__ __launch_bounds__(256) void k_fp8_amax_rc(Fp8Args a) {
+  __shared__ uint32_t part[4][kTC];
+  const int t = threadIdx.x;
+  const int64_t b = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.y * kTR, c0 = (int64_t)blockIdx.x * kTC;
+  uint4 v[kTileChunks];
+  tile_load(v, a.x + (b * a.rows + r0) * a.ld + c0, a.ld, kTR, kTC);
+#pragma unroll
+  for (int j = 0; j < kTileChunks; ++j) {
+    uint32_t m = absmax8_bits(v[j]);
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d));
+    if ((t & 15) == 0)
+      atomicMax(reinterpret_cast<unsigned int*>(a.row_max) + b * a.rows + r0 + (t >> 4) + 16 * j, m);
+  }
+  fold_col_max(v, part, a, b, r0, c0);
+}
+
 __global__ __launch_bounds__(256) void k_fp8_col_quant(Fp8Args a) {
   __shared__ uint4 lds[kTR * kTC / 8];
   __shared__ uint8_t sb[kTC];
@@ -128,6 +162,42 @@ __global__ __launch_bounds__(256) void k_fp8_col_quant(Fp8Args a) {
             r0, c0, sb);
 }
 
+// Both directions from one read of the tile: row-wise codes with the scale
+// of the row's maximum (as k_fp8_rowscale writes them) and column-wise codes
+// with the scale of the column's (as k_fp8_col_quant writes them).
+__global__ __launch_bounds__(256) void k_fp8_dual_quant(Fp8Args a) {
+  __shared__ uint4 lds[kTR * kTC / 8];
+  __shared__ uint8_t csb[kTC];
+  __shared__ uint8_t rsb[kTR];
+  const int t = threadIdx.x, cc = t & 15;
+  const int64_t b = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.y * kTR, c0 = (int64_t)blockIdx.x * kTC;
+  if (t < kTC) {
+    const int seg = row_segment(a, r0);
+    csb[t] = (uint8_t)scale_byte(reinterpret_cast<const uint32_t*>(a.work)[(b * a.segments + seg) * a.cols + c0 + t],
+                                 true);
+  } else {
+    rsb[t - kTC] = (uint8_t)scale_byte(reinterpret_cast<const uint32_t*>(a.row_max)[b * a.rows + r0 + (t - kTC)],
+                                       true);
+  }
+  uint4 v[kTileChunks];
+  tile_load(v, a.x + (b * a.rows + r0) * a.ld + c0, a.ld, kTR, kTC);
+  tile_to_lds(v, lds);
+  __syncthreads();
+  uint8_t* q = a.q + (b * a.rows + r0) * a.cols + c0 + cc * 8;
+  uint32_t* s = reinterpret_cast<uint32_t*>(a.s) + (b * (a.cols / kTC) + c0 / kTC) * a.rows + r0;
+#pragma unroll
+  for (int j = 0; j < kTileChunks; ++j) {
+    const int row = (t >> 4) + 16 * j;
+    const uint32_t sb = rsb[row];
+    *reinterpret_cast<uint2*>(q + row * a.cols) = e4m3_chunk(v[j], sb, false);
+    if (cc == 0) s[row] = sb * 0x01010101u;
+  }
+  tile_colq(lds, kTR, kTC, true,
+            TileOut{a.q_col + b * a.rows * a.cols, a.s_col + b * a.rows * (a.cols / kBlock), a.rows, a.cols, true},
+            r0, c0, csb);
+}
+
 hipError_t launch_fp8_rowscale(const Fp8Args& a, hipStream_t s) {
   dim3 grid((unsigned)((a.rows + kRowsPerGroup - 1) / kRowsPerGroup), (unsigned)a.batch);
   hipLaunchKernelGGL(k_fp8_rowscale, grid, dim3(256), 0, s, a);
@@ -140,6 +210,15 @@ hipError_t launch_fp8_colscale(const Fp8Args& a, hipStream_t s) {
   dim3 grid((unsigned)(a.cols / kTC), (unsigned)(a.rows / kTR), (unsigned)a.batch);
   hipLaunchKernelGGL(k_fp8_col_amax, grid, dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_fp8_col_quant, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_dual(const Fp8Args& a, hipStream_t s) {
+  const int64_t n = a.batch * a.segments * a.cols + a.batch * a.rows;
+  hipLaunchKernelGGL(k_fp8_clear, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0, s, a);
+  dim3 grid((unsigned)(a.cols / kTC), (unsigned)(a.rows / kTR), (unsigned)a.batch);
+  hipLaunchKernelGGL(k_fp8_amax_rc, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_fp8_dual_quant, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -83,6 +83,10 @@ struct Fp8Args {
   int32_t E;
   int64_t segments;      // column-wise: E + 1 with offsets, else 1
   int32_t* work;         // column-wise: [batch, segments, cols] int32 maxima
+  // both directions at once (launch_fp8_dual): q, s take the row-wise codes
+  uint8_t* q_col = nullptr;
+  uint8_t* s_col = nullptr;
+  int32_t* row_max = nullptr;   // [batch, rows], directly after work
 };
 
 struct PadArgs {
@@ -119,6 +123,7 @@ hipError_t launch_gemm_wgrad_hp(const GemmArgs& a, hipStream_t s);
 hipError_t launch_pad(const PadArgs& a, hipStream_t s);
 hipError_t launch_fp8_rowscale(const Fp8Args& a, hipStream_t s);
 hipError_t launch_fp8_colscale(const Fp8Args& a, hipStream_t s);
+hipError_t launch_fp8_dual(const Fp8Args& a, hipStream_t s);
 hipError_t launch_pad_map(const PadArgs& a, hipStream_t s);   // offs_pad and src_row only
 hipError_t launch_unpad(const UnpadArgs& a, hipStream_t s);
 

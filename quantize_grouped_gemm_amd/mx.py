@@ -58,6 +58,7 @@ _SIGS = {
                          _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "mx_quantize_fp8_rowwise": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "mx_quantize_fp8_colwise": ([_P, _I64, _I64, _I64, _I64, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
+    "mx_quantize_fp8_dual": ([_P, _I64, _I64, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "mx_unpad_groups": ([_P, _P, _I64, _I64, _I64, _P, _P], ctypes.c_int),
 }
 EXPORTS = tuple(_SIGS)
@@ -136,10 +137,11 @@ def quantize(x, mode="rceil", rowwise=True, colwise=False, layout="k128", out=No
     return out
 
 
-def quantize_fp8(x, rowwise=True, colwise=False, offs=None, out=None):
+def quantize_fp8(x, rowwise=True, colwise=False, offs=None, out=None, fused=True):
     """FP8 with one power-of-two scale per row (column-wise: per column, or
     per column and group with offs). x bf16 [..., R, C]; returns the same
-    keys and k128 layouts as quantize()."""
+    keys and k128 layouts as quantize(). Both directions go through the
+    one-read-per-pass entry point unless fused=False."""
     assert x.dtype == torch.bfloat16 and x.stride(-1) == 1
     R, C = x.shape[-2], x.shape[-1]
     lead = tuple(x.shape[:-2])
@@ -150,6 +152,18 @@ def quantize_fp8(x, rowwise=True, colwise=False, offs=None, out=None):
     assert batch == 1 or x.stride(-3) == R * ld
     out = dict(out or {})
     dev = x.device
+    E = 0 if offs is None else offs.shape[0]
+    if rowwise and colwise and fused:
+        out.setdefault("q_row", _u8(lead + (R, C), dev))
+        out.setdefault("s_row", _u8(lead + scale_shape(R, C), dev))
+        out.setdefault("q_col", _u8(lead + (C, R), dev))
+        out.setdefault("s_col", _u8(lead + scale_shape(C, R), dev))
+        work = torch.empty((batch * ((E + 1) * C + R),), dtype=torch.int32, device=dev)
+        st = lib().mx_quantize_fp8_dual(_ptr(x), batch, R, C, ld, _ptr(offs), E, _ptr(out["q_row"]),
+                                        _ptr(out["s_row"]), _ptr(out["q_col"]), _ptr(out["s_col"]), _ptr(work),
+                                        _stream(dev))
+        _check(st, "mx_quantize_fp8_dual")
+        return out
     if rowwise:
         out.setdefault("q_row", _u8(lead + (R, C), dev))
         out.setdefault("s_row", _u8(lead + scale_shape(R, C), dev))
@@ -159,7 +173,6 @@ def quantize_fp8(x, rowwise=True, colwise=False, offs=None, out=None):
     if colwise:
         out.setdefault("q_col", _u8(lead + (C, R), dev))
         out.setdefault("s_col", _u8(lead + scale_shape(C, R), dev))
-        E = 0 if offs is None else offs.shape[0]
         work = torch.empty((batch * (E + 1) * C,), dtype=torch.int32, device=dev)
         st = lib().mx_quantize_fp8_colwise(_ptr(x), batch, R, C, ld, _ptr(offs), E, _ptr(out["q_col"]),
                                            _ptr(out["s_col"]), _ptr(work), _stream(dev))

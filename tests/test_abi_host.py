@@ -30,7 +30,7 @@ def _declared():
 def test_header_symbols_exported_and_bound():
     L = _lib()
     names = _declared()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(L, n), n
     assert sorted(mx.EXPORTS) == names
@@ -69,6 +69,9 @@ def test_argument_errors_are_reported_without_device_work():
     assert L.mx_quantize_fp8_rowwise(p, 1, 64, 96, 96, p, p, None) == 2
     assert L.mx_quantize_fp8_colwise(p, 1, 96, 128, 128, None, 0, p, p, p, None) == 2
     assert L.mx_quantize_fp8_colwise(p, 1, 128, 128, 128, p, 0, p, p, p, None) == 2
+    assert L.mx_quantize_fp8_dual(p, 1, 96, 128, 128, None, 0, p, p, p, p, p, None) == 2
+    assert L.mx_quantize_fp8_dual(p, 1, 128, 128, 128, p, 0, p, p, p, p, p, None) == 2
+    assert L.mx_quantize_fp8_dual(p, 1, 128, 128, 128, None, 0, p, p, None, p, p, None) == 1
     # fused w13 + SwiGLU: H not a multiple of 128, bad mode
     assert L.mx_scaled_grouped_mm_swiglu_fwd(p, p, p, p, p, 4, 256, 96, 128, 0, p, p, p, p, p, None, None,
                                              None) == 2

@@ -60,6 +60,26 @@ def test_fp8_colwise_per_group(gpu, slots):
     np.testing.assert_array_equal(plain(host(got["s_col"])), ref["s_col"])
 
 
+@pytest.mark.parametrize("shape,slots", [((256, 384), None), ((640, 256), [256, 0, 128]),
+                                         ((2, 256, 384), None), ((1024, 128), [0, 384, 0, 512])])
+def test_fp8_dual(gpu, shape, slots):
+    """Both directions from the fused entry point: the oracle's bytes, and
+    bit for bit what the separate row-wise and column-wise calls write."""
+    b = _inputs(shape, 7 * sum(shape))
+    offs = None if slots is None else np.cumsum(slots).astype(np.int32)
+    offs_d = None if offs is None else to_dev(offs)
+    x = _bf16_dev(b)
+    got = mx.quantize_fp8(x, rowwise=True, colwise=True, offs=offs_d)
+    sep = mx.quantize_fp8(x, rowwise=True, colwise=True, offs=offs_d, fused=False)
+    ref = O.quantize_fp8_bf16(b, rowwise=True, colwise=True, segments=offs)
+    for k in ("q_row", "s_row", "q_col", "s_col"):
+        assert torch.equal(got[k], sep[k]), k
+    np.testing.assert_array_equal(host(got["q_row"]), ref["q_row"])
+    np.testing.assert_array_equal(plain(host(got["s_row"])), ref["s_row"])
+    np.testing.assert_array_equal(host(got["q_col"]), ref["q_col"])
+    np.testing.assert_array_equal(plain(host(got["s_col"])), ref["s_col"])
+
+
 def test_fp8_grouped_gemms_through_the_mx_kernels(gpu):
     """Forward and weight gradient on FP8 row-scaled operands: the MXFP8
     grouped kernels against the oracle's float64 GEMM of the dequantized
