@@ -525,10 +525,11 @@ __device__ __forceinline__ void swiglu_epilogue(const v16f (&acc)[4][4], const S
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) {
 #pragma unroll
         for (int q = 0; q < 8; ++q)
           X[(wm * 128 + (i * 4 + j) * 8 + q) * 64 + lane] = pack_bf16x2(acc[i][j][2 * q], acc[i][j][2 * q + 1]);
+      }
   }
   lds_barrier();
   if (wn == 0) {
@@ -583,8 +584,28 @@ __device__ __forceinline__ void swiglu_epilogue(const v16f (&acc)[4][4], const S
   }
 }
 
+// Stores a finished tile (and, FUSED, runs the SwiGLU epilogue on it).
+template <bool FUSED>
+__device__ __forceinline__ void finish_tile(const v16f (&acc)[4][4], const TileSpec& ts, uint8_t* st0, uint8_t* st1,
+                                            const SwigluOut* so, int64_t h_r0, int64_t h_c0) {
+  const int w = threadIdx.x >> 6;
+  if (direct_epilogue(ts)) {
+    if (ts.out_f32)
+      store_tile_direct<true>(acc, ts);
+    else
+      store_tile_direct<false>(acc, ts);
+  } else {
+    wg_barrier();   // every wave is done with the stage buffers
+    uint8_t* mine = (w & 1 ? st1 : st0) + (w >> 1) * kEpiWaveBytes;
+    store_tile(acc, ts, mine);
+  }
+  if constexpr (FUSED) swiglu_epilogue(acc, *so, ts.valid_m, h_r0, h_c0, st1, st0);
+}
+
 // FUSED: the tile is a fused SwiGLU tile (see swiglu_epilogue); a tile
-// without K steps (the tail) then still runs the epilogue on zeros.
+// without K steps (the tail) then still runs the epilogue, on zeros. That
+// case returns on its own path, so the K loop's accumulators never merge
+// with constant zeros (the merge made the register allocator spill).
 template <bool FUSED = false>
 __device__ __forceinline__ void gemm_tile(const TileSpec& tile, const SwigluOut* so = nullptr, int64_t h_r0 = 0,
                                           int64_t h_c0 = 0) {
@@ -592,11 +613,18 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& tile, const SwigluOut*
   __shared__ __align__(16) uint8_t st0[kStageBytes];
   __shared__ __align__(16) uint8_t st1[kStageBytes];
   __shared__ __align__(16) uint8_t sink[256];
-  if constexpr (!FUSED) {
-    if (ts.nk <= 0) {
+  if (ts.nk <= 0) {
+    if constexpr (FUSED) {
+      v16f zero[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) zero[i][j] = v16f{};
+      finish_tile<true>(zero, ts, st0, st1, so, h_r0, h_c0);
+    } else {
       zero_tile(ts);
-      return;
     }
+    return;
   }
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -640,7 +668,6 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& tile, const SwigluOut*
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
   const int nk = ts.nk;
-  if (!FUSED || nk > 0) {
   const int last = nk - 1;
   // prologue: steps 0 and 1 to LDS, each DMA followed by two prefetch loads
   // (steps 2 and 3; past the end, the last step stands in)
@@ -662,18 +689,7 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& tile, const SwigluOut*
   }
   if (ks < nk) step_full(d, ks, nk, st0, st1, r, acc, wm, wn, lane, sink);
   MX_WAIT_VM_LDS(0);
-  }
-  if (direct_epilogue(ts)) {
-    if (ts.out_f32)
-      store_tile_direct<true>(acc, ts);
-    else
-      store_tile_direct<false>(acc, ts);
-  } else {
-    wg_barrier();   // every wave is done with the stage buffers
-    uint8_t* mine = (w & 1 ? st1 : st0) + (w >> 1) * kEpiWaveBytes;
-    store_tile(acc, ts, mine);
-  }
-  if constexpr (FUSED) swiglu_epilogue(acc, *so, ts.valid_m, h_r0, h_c0, st1, st0);
+  finish_tile<FUSED>(acc, ts, st0, st1, so, h_r0, h_c0);
 }
 
 // ---------------------------------------------------------------- bf16 wgrad
