@@ -337,7 +337,8 @@ def _vendor_gemm_component(torch, dev, reps=10):
 
 def _cpu_baseline():
     """The oracle on a bounded slice of the default workload: one expert with
-    1024 of its 8192 hidden units and 128 tokens. Weight quantization and the
+    4096 of its 8192 hidden units and 1024 tokens (about 15 s on 16 host
+    threads). Weight quantization and the
     token-dependent work are timed separately and each scaled to the full
     step (16 experts x 8192 hidden; 16384 tokens x 8192 hidden)."""
     import numpy as np
@@ -348,7 +349,7 @@ def _cpu_baseline():
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    E, T, D, Hs = 1, 128, 5120, 1024
+    E, T, D, Hs = 1, 1024, 5120, 4096
     c = synth.MOE_SCOUT
     x, w1, w3, w2, dy = [synth.bits(t) for t in synth.mlp_inputs(T, D, Hs, E=E, seed=0)]
     w13 = np.concatenate([w1, w3], axis=1)
@@ -433,6 +434,11 @@ def main():
     if not args.no_components:
         comp = {"quantize_stress_32768x7168": _quant_component(torch, dev),
                 "linear_256x256x512": _linear_component(torch, dev)}
+        try:
+            comp["dense_gemm_vs_vendor"] = _vendor_gemm_component(torch, dev, reps=5)
+        except Exception as e:   # the vendor library's GEMMs are context, not part of the path
+            comp["dense_gemm_vs_vendor"] = f"unavailable: {type(e).__name__}: {str(e)[:120]}"
+        torch.cuda.empty_cache()
         if name == "moe_scout":
             comp["moe_scout_w13_fwd_fused_swiglu"] = _fused_swiglu_component(torch, dev)
         if name.startswith("moe"):
