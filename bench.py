@@ -178,15 +178,28 @@ def _kernel_table(stages, per):
     return out, table
 
 
-def _roofline_gemm(table, kernel, peak, traffic=None):
+def _roofline_gemm(table, kernel, peak, traffic=None, padded_ratio=None):
+    """Useful flops (real tokens) per launch over the launch time; with
+    padded_ratio (padded tokens / real tokens) also the rate over the
+    padded groups the kernel multiplies."""
     e = table[kernel]
     achieved = e["flops"] / e["seconds"]       # per-launch flops / per-launch time, averaged
     r = {"kernel": kernel, "bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": peak / 1e12,
          "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
          "per_launch_flops": e["flops"] / e["launches"], "avg_launch_us": round(e["seconds"] / e["launches"] * 1e6, 2)}
+    if padded_ratio is not None:
+        r["padded_tflops"] = round(achieved * padded_ratio / 1e12, 1)
     if traffic is not None:
         r["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)"
     return r
+
+
+def _padded_ratio(config):
+    """Tokens after padding each group to 128, over real tokens (MoE only)."""
+    sizes = config.get("group_sizes")
+    if not sizes:
+        return None
+    return sum(-(-n // 128) * 128 for n in sizes) / sum(sizes)
 
 
 def _quant_component(torch, dev, reps=10):
@@ -363,6 +376,7 @@ def _cpu_baseline():
     t_tok = max(t_all - t_w, 1e-9)
     full = t_w * c["E"] * (c["H"] / Hs) + t_tok * (c["T"] / T) * (c["H"] / Hs)
     return {"value": round(c["T"] / full, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
             "sample": (f"oracle on 1 expert x {Hs}/{c['H']} hidden x {T} tokens, D={D}: weight dual "
                        f"quantization {t_w:.1f} s and token work {t_tok:.1f} s, scaled to 16 experts x "
                        f"{c['H']} hidden and {c['T']} tokens (estimated full step {full:.0f} s)"),
@@ -424,7 +438,8 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, routed group sizes)",
         "config": config,
         "roofline": _roofline_gemm(table, gemm_kernel, PEAK_MXFP8,
-                                   _measured_traffic() if name == "moe_scout" else None),
+                                   _measured_traffic() if name == "moe_scout" else None,
+                                   _padded_ratio(config)),
         "step_roofline": {"gemm_useful_tflops": round(gemm_flops / gemm_time / 1e12, 1),
                           "ideal_ms": round(roof_time * 1e3, 4), "frac": round(roof_time / wall, 4)},
         "kernels": kernels,
@@ -467,7 +482,7 @@ def main():
             k2, t2 = _kernel_table(s2, p2)
             gk = "k_gemm_grouped" if other.startswith("moe") else "k_gemm_dense"
             comp[other] = {"tokens_per_s": round(tok2 / w2_, 1), "ms_per_step": round(w2_ * 1e3, 3),
-                           "gemm_roofline": _roofline_gemm(t2, gk, PEAK_MXFP8), "kernels": k2,
+                           "gemm_roofline": _roofline_gemm(t2, gk, PEAK_MXFP8, padded_ratio=_padded_ratio(c2)), "kernels": k2,
                            "workload": c2["workload"]}
             del n2, a2, s2
             torch.cuda.empty_cache()
