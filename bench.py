@@ -204,19 +204,21 @@ def _padded_ratio(config):
 
 def _quant_component(torch, dev, reps=10):
     """MX dual (row + column) and row-only quantization of the [32768, 7168]
-    stress tensor, RCEIL; a 1 GiB buffer is overwritten between launches so
-    the tensor is read from HBM, not the last-level cache."""
+    stress tensor, RCEIL. A 1 GiB buffer is read between launches, so the
+    tensor comes from HBM, not the last-level cache. The flush reads rather
+    than writes: a written buffer leaves its dirty lines in L2 and the
+    last-level cache, and the timed kernel would pay for their write-back."""
     from quantize_grouped_gemm_amd import mx, synth
     R, C = synth.STRESS_SHAPE
     x = synth.stress_tensor(R, C, seed=0, device=dev)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
     res = {}
     for label, row, col in (("dual", True, True), ("rowwise", True, False), ("colwise", False, True)):
         out = mx.quantize(x, "rceil", row, col)
         nbytes = R * C * (2 + (int(row) + int(col)) * (1 + 1 / 32))
         ts = []
         for _ in range(reps):
-            flush.zero_()
+            flush.sum()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             mx.quantize(x, "rceil", row, col, out=out)

@@ -126,9 +126,16 @@ def stress_tensor(R=STRESS_SHAPE[0], C=STRESS_SHAPE[1], seed=0, device="cpu"):
     flat = x.view(-1)
     n = R * C
 
+    def last_wins(idx):
+        # positions drawn twice keep the later value; a parallel scatter would
+        # pick either, so duplicates are resolved here, before it
+        _, rev = np.unique(idx[::-1], return_index=True)
+        return idx.size - 1 - rev
+
     def put(idx, vals):
-        flat[torch.as_tensor(idx, device=device)] = torch.as_tensor(
-            vals, dtype=torch.float32, device=device)
+        keep = last_wins(idx)
+        flat[torch.as_tensor(idx[keep], device=device)] = torch.as_tensor(
+            np.asarray(vals)[keep], dtype=torch.float32, device=device)
 
     k = max(1, n // 1000)
     idx = rng.integers(0, n, k)
@@ -165,7 +172,9 @@ def stress_tensor(R=STRESS_SHAPE[0], C=STRESS_SHAPE[1], seed=0, device="cpu"):
         return torch.as_tensor(v, device=device)
 
     k2 = max(1, n // 10000)
-    xi[torch.as_tensor(rng.integers(0, n, k2), device=device)] = sub_bits(k2)
+    idx = rng.integers(0, n, k2)
+    keep = last_wins(idx)
+    xi[torch.as_tensor(idx[keep], device=device)] = sub_bits(k2)[torch.as_tensor(keep, device=device)]
     xi2 = xi.view(R, C)
     r, b = row_blocks(16)
     for i in range(16):
@@ -177,7 +186,8 @@ def stress_tensor(R=STRESS_SHAPE[0], C=STRESS_SHAPE[1], seed=0, device="cpu"):
     # exactly +-448 (bf16 0x43E0)
     idx = rng.integers(0, n, k2)
     v448 = np.where(rng.integers(0, 2, k2) == 1, 0xC3E0, 0x43E0).astype(np.uint16).view(np.int16)
-    xi[torch.as_tensor(idx, device=device)] = torch.as_tensor(v448, device=device)
+    keep = last_wins(idx)
+    xi[torch.as_tensor(idx[keep], device=device)] = torch.as_tensor(v448[keep], device=device)
 
     def exp_bits(kk, mant):
         # bf16 with exponent field 127 + kk and 7-bit mantissa ``mant``
