@@ -33,6 +33,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.0f) & 0xFFFFu; }
 
+// 16-byte global load marked non-temporal (data streamed through once).
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u q = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(q.x, q.y, q.z, q.w);
+}
+
 // max |v| over the 8 bf16 values of a 16-byte chunk, as 15-bit magnitude bits
 // (non-negative bf16 bit patterns order like their values; NaN > 0x7F80).
 __device__ __forceinline__ uint32_t absmax8_bits(uint4 v) {

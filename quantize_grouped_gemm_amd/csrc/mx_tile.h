@@ -59,7 +59,9 @@ __device__ __forceinline__ void tile_rowq(const uint4 (&v)[kTileChunks], int row
 }
 
 // Loads the thread's chunks of a bf16 tile whose (0,0) is `base` with row
-// stride ld elements; chunks outside the valid region read as zero.
+// stride ld elements; chunks outside the valid region read as zero. NT:
+// non-temporal loads (see kStreamBytes in mx_quant.hip for when).
+template <bool NT = false>
 __device__ __forceinline__ void tile_load(uint4 (&v)[kTileChunks], const uint16_t* base,
                                           int64_t ld, int rows_valid, int cols_valid) {
   const int t = threadIdx.x;
@@ -68,7 +70,8 @@ __device__ __forceinline__ void tile_load(uint4 (&v)[kTileChunks], const uint16_
   for (int j = 0; j < kTileChunks; ++j) {
     const int row = (t >> 4) + 16 * j;
     v[j] = (row < rows_valid && cc * 8 < cols_valid)
-               ? *reinterpret_cast<const uint4*>(base + row * ld + cc * 8)
+               ? (NT ? load_stream16(base + row * ld + cc * 8)
+                     : *reinterpret_cast<const uint4*>(base + row * ld + cc * 8))
                : make_uint4(0, 0, 0, 0);
   }
 }

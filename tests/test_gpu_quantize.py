@@ -139,6 +139,41 @@ def test_stress_full_size_sampled(gpu, mode):
     np.testing.assert_array_equal(host(deq[ri]).view(np.uint32), ref.view(np.uint32))
 
 
+def test_quantize_inputs_over_one_gib(gpu):
+    """Inputs of 1 GiB and more are read with plain loads, smaller ones with
+    non-temporal loads: a [2, 16512, 16384] batch of expert weights (1.01
+    GiB, N(0, 0.02) with planted outliers and zero blocks) quantized both
+    ways, checked bit-exactly on sampled rows and columns of each matrix,
+    and against the same matrices quantized one at a time (0.50 GiB each)."""
+    Bt, R, C = 2, 16512, 16384
+    assert Bt * R * C * 2 >= 1 << 30 > R * C * 2
+    g = synth.generator(21, dev())
+    w = synth.normal_bf16((Bt, R, C), 0.02, g, dev())
+    rng = np.random.default_rng(21)
+    flat = w.view(-1)
+    pos = torch.as_tensor(np.unique(rng.integers(0, w.numel(), 4096)), device=dev())
+    flat[pos] = torch.as_tensor(rng.choice([-1.0, 1.0], len(pos)) * 2.0 ** rng.integers(-3, 9, len(pos)),
+                                dtype=torch.bfloat16, device=dev())
+    w[0, 100, 32 * 7:32 * 8] = 0
+    w[1, 32 * 9:32 * 10, 5] = 0
+    got = mx.quantize(w, "rceil", True, True)
+    for b in range(Bt):
+        one = mx.quantize(w[b], "rceil", True, True)
+        for k in ("q_row", "s_row", "q_col", "s_col"):
+            assert torch.equal(got[k][b], one[k]), f"{k} of matrix {b}"
+        # row 100 holds matrix 0's zero row block, column 5 matrix 1's zero column block
+        rows = np.unique(np.append(rng.choice(R, 64, replace=False), 100))
+        cols = np.unique(np.append(rng.choice(C, 64, replace=False), 5))
+        ri = torch.as_tensor(rows, device=dev())
+        ci = torch.as_tensor(cols, device=dev())
+        q, s = O.quantize(O.bf16_to_f64(bf16_host(w[b][ri])), "rceil")
+        np.testing.assert_array_equal(host(got["q_row"][b][ri]), q)
+        np.testing.assert_array_equal(plain(host(got["s_row"][b]))[rows], s)
+        q, s = O.quantize(O.bf16_to_f64(bf16_host(w[b][:, ci])).T, "rceil")
+        np.testing.assert_array_equal(host(got["q_col"][b][ci]), q)
+        np.testing.assert_array_equal(plain(host(got["s_col"][b]))[cols], s)
+
+
 @pytest.mark.parametrize("layout", ["plain", "k128"])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_dequantize_all_codes_all_scales(gpu, out_dtype, layout):
