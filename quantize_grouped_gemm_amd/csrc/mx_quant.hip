@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kTileThreads) void k_swiglu_fwd(SwigluFwdArgs a) {
 // dA = dh*b*s*(1 + a*(1-s)), dB = dh*a*s with s = sigmoid(a), float32.
 __device__ __forceinline__ void swiglu_grad_f32(float dh, float a, float b, float& da,
                                                 float& db) {
-  const float s = 1.0f / (1.0f + expf(-a));
+  const float s = sigmoid_f32(a);
   da = (dh * b) * (s * (1.0f + a * (1.0f - s)));
   db = dh * (a * s);
 }
