@@ -61,6 +61,23 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   return v;
 }
 
+// OR of v over lanes l, l + 4, l + 8, l + 12 of each 16-lane row (DPP
+// row_ror:4 then row_ror:8). Every lane of the row must be active.
+__device__ __forceinline__ uint32_t or_row_quarters(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false);
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
+  return v;
+}
+
+// OR of v over the lanes l, l ^ 2, 7 - l, (7 - l) ^ 2 of each 8-lane group,
+// which include one lane of each pair {2k, 2k + 1} (DPP quad_perm [2,3,0,1]
+// then row_half_mirror). Every lane of the group must be active.
+__device__ __forceinline__ uint32_t or_octet_pairs(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);
+  return v;
+}
+
 // ---------------------------------------------------------------- scales
 
 // E8M0 scale byte (E + 127) of a block whose max magnitude has bf16 bits

@@ -27,7 +27,8 @@ struct TileOut {
 // Row-wise quantization of the thread's 8 chunks. The tile's (0,0) sits at
 // row r0, column c0 of the output. All lanes must reach this function. In the
 // k128 layout (c0 % 128 == 0) a row's four block scales form one dword: the
-// 16 lanes of the row gather it with two lane swaps and one lane stores it.
+// 16 lanes of the row gather it with two DPP row rotations and one lane
+// stores it.
 __device__ __forceinline__ void tile_rowq(const uint4 (&v)[kTileChunks], int rows_valid,
                                           int cols_valid, bool rceil, TileOut o, int64_t r0,
                                           int64_t c0) {
@@ -41,9 +42,7 @@ __device__ __forceinline__ void tile_rowq(const uint4 (&v)[kTileChunks], int row
     const uint2 codes = e4m3_chunk(v[j], sb, !rceil);
     uint32_t packed = 0;
     if (o.k128) {
-      packed = sb << (8 * (cc >> 2));
-      packed |= (uint32_t)__shfl_xor((int)packed, 4);
-      packed |= (uint32_t)__shfl_xor((int)packed, 8);
+      packed = or_row_quarters(sb << (8 * (cc >> 2)));
     }
     if (row < rows_valid && colok) {
       const int64_t orow = r0 + row;
@@ -146,12 +145,8 @@ __device__ __forceinline__ void tile_colq(const uint4* lds4, int rows_valid, int
     // scale bytes of the step's four blocks for the two output rows
     uint32_t p0 = 0, p1 = 0;
     if (o.k128) {
-      p0 = sb0 << (8 * (q >> 1));
-      p1 = sb1 << (8 * (q >> 1));
-      p0 |= (uint32_t)__shfl_xor((int)p0, 2);
-      p1 |= (uint32_t)__shfl_xor((int)p1, 2);
-      p0 |= (uint32_t)__shfl_xor((int)p0, 4);
-      p1 |= (uint32_t)__shfl_xor((int)p1, 4);
+      p0 = or_octet_pairs(sb0 << (8 * (q >> 1)));
+      p1 = or_octet_pairs(sb1 << (8 * (q >> 1)));
     }
     if (2 * cp < cols_valid && 16 * q < rows_valid) {
       const int64_t orow0 = c0 + 2 * cp;
