@@ -69,6 +69,17 @@ __device__ __forceinline__ uint32_t or_row_quarters(uint32_t v) {
   return v;
 }
 
+// max of v over the 16 lanes of each DPP row (quad permutes for lanes ^ 1
+// and ^ 2, then row_ror:4 and row_ror:8). Every lane of the row must be
+// active.
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));
+  return v;
+}
+
 // OR of v over the lanes l, l ^ 2, 7 - l, (7 - l) ^ 2 of each 8-lane group,
 // which include one lane of each pair {2k, 2k + 1} (DPP quad_perm [2,3,0,1]
 // then row_half_mirror). Every lane of the group must be active.

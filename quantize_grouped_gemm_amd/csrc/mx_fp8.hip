@@ -42,8 +42,7 @@ __global__ __launch_bounds__(256) void k_fp8_rowscale(Fp8Args a) {
   if (ok)
     for (int it = 0; it < steps; ++it)
       m = max(m, absmax8_bits(*reinterpret_cast<const uint4*>(x + it * 128 + cc * 8)));
-#pragma unroll
-  for (int d = 1; d < 16; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d));
+  m = row16_max(m);
   const uint32_t sb = scale_byte(m, true);
   if (!ok) return;
   uint8_t* q = a.q + (b * a.rows + row) * a.cols;
@@ -134,9 +133,7 @@ __global__ __launch_bounds__(256) void k_fp8_amax_rc(Fp8Args a) {
   tile_load(v, a.x + (b * a.rows + r0) * a.ld + c0, a.ld, kTR, kTC);
 #pragma unroll
   for (int j = 0; j < kTileChunks; ++j) {
-    uint32_t m = absmax8_bits(v[j]);
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d));
+    const uint32_t m = row16_max(absmax8_bits(v[j]));
     if ((t & 15) == 0)
       atomicMax(reinterpret_cast<unsigned int*>(a.row_max) + b * a.rows + r0 + (t >> 4) + 16 * j, m);
   }
