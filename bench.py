@@ -228,7 +228,26 @@ def _quant_component(torch, dev, reps=10):
         t = sorted(ts)[len(ts) // 2]
         res[label] = {"us": round(t * 1e6, 1), "gbps": round(nbytes / t / 1e9, 1),
                       "frac_hbm": round(nbytes / t / PEAK_HBM, 3)}
-    del x, flush
+    # dequantization of the row-wise codes (the round trip's second half):
+    # 1 + 1/32 B read, 2 B (bf16) or 4 B (float32) written per element
+    q = mx.quantize(x, "rceil", True, False)
+    for label, dt, esz in (("dequant_bf16", torch.bfloat16, 2), ("dequant_f32", torch.float32, 4)):
+        out = mx.dequantize(q["q_row"], q["s_row"], dt)
+        nbytes = R * C * (1 + 1 / 32 + esz)
+        ts = []
+        for _ in range(reps):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            mx.dequantize(q["q_row"], q["s_row"], dt, out=out)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        t = sorted(ts)[len(ts) // 2]
+        res[label] = {"us": round(t * 1e6, 1), "gbps": round(nbytes / t / 1e9, 1),
+                      "frac_hbm": round(nbytes / t / PEAK_HBM, 3)}
+        del out
+    del x, flush, q
     return res
 
 

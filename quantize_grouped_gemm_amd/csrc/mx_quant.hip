@@ -171,40 +171,53 @@ __global__ __launch_bounds__(kTileThreads) void k_swiglu_bwd(SwigluBwdArgs a) {
 
 // ---------------------------------------------------------------- dequantize
 
-// Thread per 16 codes (a half block): one 16-byte code load, one scale byte.
-__global__ __launch_bounds__(256) void k_dequant(DequantArgs a) {
-  const int64_t n16 = a.rows * a.cols / 16;
+// Each thread converts the codes behind one 16-byte output store (8 codes to
+// bf16, 4 to float32), so the lanes of a store instruction write 1 KB of
+// consecutive bytes; it loads those codes (8 or 4 bytes, also consecutive
+// across lanes) and their block's scale byte. Chunk i (kCodes codes) is row
+// i / (cols / kCodes); the quotient comes from a precomputed multiplier
+// (FastDiv, 32-bit) when the chunk count fits 32 bits, from 64-bit
+// division otherwise (IDX64).
+template <bool F32, bool IDX64>
+__global__ __launch_bounds__(256) void k_dequant(DequantArgs a, FastDiv per_row) {
+  constexpr int kCodes = F32 ? 4 : 8;
+  const int64_t per = a.cols / kCodes;
+  const int64_t n = a.rows * per;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
-    const uint4 c = *reinterpret_cast<const uint4*>(a.q + 16 * i);
-    uint32_t sb;
-    if (a.k128) {
-      const int64_t r = (16 * i) / a.cols, blk = ((16 * i) % a.cols) >> 5;
-      sb = a.s[((blk >> 2) * a.rows + r) * 4 + (blk & 3)];
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    uint32_t w[kCodes / 4];
+    if constexpr (F32) {
+      w[0] = *reinterpret_cast<const uint32_t*>(a.q + 4 * i);
     } else {
-      sb = a.s[i >> 1];
+      const uint2 c = *reinterpret_cast<const uint2*>(a.q + 8 * i);
+      w[0] = c.x;
+      w[1] = c.y;
     }
-    uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    float f[16];
+    int64_t r, cc;
+    if constexpr (IDX64) {
+      r = i / per;
+      cc = i - r * per;
+    } else {
+      const uint32_t rr = fdiv((uint32_t)i, per_row);
+      r = rr;
+      cc = (int64_t)((uint32_t)i - rr * per_row.d);
+    }
+    const int64_t blk = (cc * kCodes) >> 5;
+    const uint32_t sb = a.k128 ? a.s[((blk >> 2) * a.rows + r) * 4 + (blk & 3)] : a.s[r * (a.cols / 32) + blk];
+    float f[kCodes];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < kCodes; ++k) {
       const float v = e4m3_value((w[k >> 2] >> (8 * (k & 3))) & 0xFFu);
       // v has at most 4 significant bits and |v| >= 2^-9, so v * 2^(sb-127)
       // is exact in float32 down to 2^-136 (a float32 subnormal); only
       // E = 127 with |v| > 1 overflows, to infinity
       f[k] = sb == 0xFFu ? __uint_as_float(0x7FC00000u) : ldexpf(v, (int)sb - 127);
     }
-    if (a.out_f32) {
-      float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + 16 * i);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) o[k] = make_float4(f[4 * k], f[4 * k + 1], f[4 * k + 2], f[4 * k + 3]);
-    } else {
-      uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + 16 * i);
-      o[0] = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                        pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
-      o[1] = make_uint4(pack_bf16x2(f[8], f[9]), pack_bf16x2(f[10], f[11]),
-                        pack_bf16x2(f[12], f[13]), pack_bf16x2(f[14], f[15]));
-    }
+    if constexpr (F32)
+      reinterpret_cast<float4*>(a.out)[i] = make_float4(f[0], f[1], f[2], f[3]);
+    else
+      reinterpret_cast<uint4*>(a.out)[i] = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                                     pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
   }
 }
 
@@ -254,12 +267,24 @@ hipError_t launch_swiglu_bwd(const SwigluBwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {
-  const int64_t n16 = a.rows * a.cols / 16;
-  if (n16 == 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>((n16 + 255) / 256, 256 * 64);
-  hipLaunchKernelGGL(k_dequant, dim3((unsigned)blocks), dim3(256), 0, s, a);
+template <bool F32>
+static hipError_t launch_dequant_t(const DequantArgs& a, hipStream_t s) {
+  constexpr int kCodes = F32 ? 4 : 8;
+  const int64_t n = a.rows * a.cols / kCodes;
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 256 * 64);
+  // the grid-stride index stays below n + grid size; 32-bit quotients need
+  // that below 2^32
+  if (n + blocks * 256 < ((int64_t)1 << 32))
+    hipLaunchKernelGGL((k_dequant<F32, false>), dim3((unsigned)blocks), dim3(256), 0, s, a,
+                       make_fastdiv((uint32_t)(a.cols / kCodes)));
+  else
+    hipLaunchKernelGGL((k_dequant<F32, true>), dim3((unsigned)blocks), dim3(256), 0, s, a, FastDiv{});
   return hipGetLastError();
+}
+
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {
+  return a.out_f32 ? launch_dequant_t<true>(a, s) : launch_dequant_t<false>(a, s);
 }
 
 }  // namespace mxk
