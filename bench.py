@@ -54,19 +54,42 @@ def gemm_source_hash():
     return h.hexdigest()
 
 
+# MFMA-busy fraction and engine clock of the dominant kernel, from a
+# rocprofv3 pass over SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE (see the
+# file); same source-hash rule.
+MFMA_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_utilization_moe_scout.md")
+
+
+def _profile_values(path):
+    """The "key: value" lines of a profile summary, or None if its counters
+    were taken on other GEMM sources."""
+    try:
+        kv = {}
+        for line in open(path):
+            if ":" in line and not line.startswith(("#", " ", "|", "-")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        return kv if kv.get("source_sha256") == gemm_source_hash() else None
+    except OSError:
+        return None
+
+
 def _measured_traffic():
     """Bytes per launch of k_gemm_grouped on the default workload, or None if
     the counters were taken on other kernel sources."""
     try:
-        kv = {}
-        for line in open(TRAFFIC_FILE):
-            if ":" in line and not line.startswith(("#", " ", "|", "-")):
-                k, v = line.split(":", 1)
-                kv[k.strip()] = v.strip()
-        if kv.get("source_sha256") != gemm_source_hash():
-            return None
-        return float(kv["traffic_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+        return float(_profile_values(TRAFFIC_FILE)["traffic_bytes_per_launch"])
+    except (TypeError, KeyError, ValueError):
+        return None
+
+
+def _measured_mfma():
+    """MFMA-busy fraction and engine clock (GHz) of k_gemm_grouped's launches
+    on the default workload, or None."""
+    try:
+        kv = _profile_values(MFMA_FILE)
+        return {"mfma_busy": float(kv["mfma_busy_per_launch"]), "sclk_ghz": float(kv["sclk_ghz_per_launch"])}
+    except (TypeError, KeyError, ValueError):
         return None
 
 
@@ -178,10 +201,12 @@ def _kernel_table(stages, per):
     return out, table
 
 
-def _roofline_gemm(table, kernel, peak, traffic=None, padded_ratio=None):
+def _roofline_gemm(table, kernel, peak, traffic=None, padded_ratio=None, mfma=None):
     """Useful flops (real tokens) per launch over the launch time; with
     padded_ratio (padded tokens / real tokens) also the rate over the
-    padded groups the kernel multiplies."""
+    padded groups the kernel multiplies. mfma: the profiled MFMA-busy
+    fraction and engine clock of the kernel (the published peak assumes the
+    2.4 GHz peak clock)."""
     e = table[kernel]
     achieved = e["flops"] / e["seconds"]       # per-launch flops / per-launch time, averaged
     r = {"kernel": kernel, "bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": peak / 1e12,
@@ -191,6 +216,9 @@ def _roofline_gemm(table, kernel, peak, traffic=None, padded_ratio=None):
         r["padded_tflops"] = round(achieved * padded_ratio / 1e12, 1)
     if traffic is not None:
         r["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)"
+    if mfma is not None:
+        r["mfma_busy_profiled"] = mfma["mfma_busy"]
+        r["sclk_ghz_profiled"] = mfma["sclk_ghz"]
     return r
 
 
@@ -479,7 +507,7 @@ def main():
         "config": config,
         "roofline": _roofline_gemm(table, gemm_kernel, PEAK_MXFP8,
                                    _measured_traffic() if name == "moe_scout" else None,
-                                   _padded_ratio(config)),
+                                   _padded_ratio(config), _measured_mfma() if name == "moe_scout" else None),
         "step_roofline": {"gemm_useful_tflops": round(gemm_flops / gemm_time / 1e12, 1),
                           "ideal_ms": round(roof_time * 1e3, 4), "frac": round(roof_time / wall, 4)},
         "kernels": kernels,
