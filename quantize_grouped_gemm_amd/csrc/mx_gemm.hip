@@ -30,12 +30,13 @@
 // of 16, so the pass is free of bank conflicts (and so are 8-lane groups).
 //
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs, each
-// with its own L2. Tiles are numbered in bands of 8 row tiles (column tiles
-// walked within a band), and the dense and grouped kernels deal chunks of 32
-// consecutive tiles to the XCDs round-robin, so the 32 workgroups resident
-// on one XCD share A and B tiles while every XCD gets a spread of the tile
-// order. The weight-gradient kernel gives each XCD an equal contiguous share
-// of every group instead (its groups run one after another).
+// with its own L2. Tiles are numbered in bands of a few row tiles (column
+// tiles walked within a band), and the dense and grouped kernels deal chunks
+// of 16 consecutive tiles to the XCDs round-robin, so the workgroups
+// resident on one XCD share A and B tiles while every XCD gets a spread of
+// the tile order. The weight-gradient kernel gives each XCD an equal
+// contiguous share of every group instead (its groups run one after
+// another). Band heights and chunk sizes are per kernel (kOrderDense ...).
 //
 // MFMA operand layout (32x32x64, 8-bit elements, measured on the device):
 // lane l holds row (l & 31) of its 32-row block; with h = l >> 5 its bytes
@@ -60,7 +61,17 @@ constexpr int kStageA = kBM * kBK;                       // 32 KB of A codes per
 constexpr int kStageB = kBN * kBK;                       // 32 KB of B codes
 constexpr int kStageS = (kBM + kBN) * 4;                 // scale dwords of A and B (2 KB)
 constexpr int kStageBytes = kStageA + kStageB + kStageS;
-constexpr int kBandM = 8;                                // row tiles per band of the tile order
+// Tile order per kernel: row tiles per band, tiles per XCD chunk (dense and
+// grouped) and column tiles sharing an A row tile's L2 prefetch. Chosen by
+// paired runs on MI355X over band heights 1-16 and chunks 16-64: against
+// bands of 8 and chunks of 32, the MoE Scout step took 2.8% less time, the
+// dense and DeepSeek-V3-like steps 0.4-1%.
+struct TileOrder {
+  int band, chunk, a_share;
+};
+constexpr TileOrder kOrderDense{4, 16, 4};
+constexpr TileOrder kOrderGrouped{2, 16, 8};
+constexpr TileOrder kOrderWgrad{4, 0, 4};
 constexpr int kMaxGroups = 1024;                         // group table lives in LDS
 #ifndef MX_GEMM_PREFETCH
 #define MX_GEMM_PREFETCH 1
@@ -882,48 +893,51 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   return xcd * per + min(xcd, rem) + j;
 }
 
-// Deals tiles [0, total) to the 8 XCDs in chunks of kXcdChunk consecutive
+// Deals tiles [0, total) to the 8 XCDs in chunks of CHUNK consecutive
 // tiles, round-robin: chunk k is XCD (k % 8)'s (k / 8)-th chunk. Workgroup b
 // (dispatched to XCD b % 8 as that XCD's (b >> 3)-th) gets its XCD's
 // (b >> 3)-th tile, or -1 past the end. Used where tile costs vary across
 // the tile order (grouped GEMMs: a band holding several small groups loads
-// more distinct B tiles), so that no XCD's share is all slow tiles. A chunk
-// is one round of the XCD's 32 CUs, so tiles running together still share
-// their band's A and B tiles in that XCD's L2.
-constexpr int kXcdChunk = 32;
-
+// more distinct B tiles), so that no XCD's share is all slow tiles. The
+// XCD's 32 CUs run two chunks at a time, so tiles running together still
+// share A and B tiles in that XCD's L2.
+template <int CHUNK>
 __device__ __forceinline__ int xcd_chunked(int b, int total) {
   const int x = b & 7, j = b >> 3;
-  const int t = ((j / kXcdChunk) * 8 + x) * kXcdChunk + j % kXcdChunk;
+  const int t = ((j / CHUNK) * 8 + x) * CHUNK + j % CHUNK;
   return t < total ? t : -1;
 }
 
 // Workgroup indices the chunked deal of `total` tiles spans.
+template <int CHUNK>
 __host__ __device__ constexpr int64_t xcd_chunked_span(int64_t total) {
-  return (total + 8 * kXcdChunk - 1) / (8 * kXcdChunk) * (8 * kXcdChunk);
+  return (total + 8 * CHUNK - 1) / (8 * CHUNK) * (8 * CHUNK);
 }
 
-// Tile index -> (row tile, column tile) in bands of kBandM row tiles, column
+// Tile index -> (row tile, column tile) in bands of BAND row tiles, column
 // tiles walked within a band. `first` and `rows` return the band.
+template <int BAND>
 __device__ __forceinline__ void band_order(int t, int mt, int nt, int& m, int& n, int& first, int& rows) {
-  const int band = t / (kBandM * nt);
-  first = band * kBandM;
-  rows = min(kBandM, mt - first);
-  const int r = t - band * kBandM * nt;
+  const int band = t / (BAND * nt);
+  first = band * BAND;
+  rows = min(BAND, mt - first);
+  const int r = t - band * BAND * nt;
   m = first + r % rows;
   n = r / rows;
 }
 
 // Prefetch shares. Workgroups running together on an XCD hold consecutive
-// tile indices: up to kBandM row tiles of one band times about 4 column
-// tiles. An A row tile is thus shared by ~4 column tiles: column tile n takes
-// rows 64 (n % 4) .. + 63. A B column tile is shared by the `cnt` row tiles
-// of the band that use the same B (all of the band, or in a grouped GEMM the
-// band's tiles of one group); the row tile at position `idx` among them takes
-// the idx-th of cnt equal slices of its rows.
+// tile indices: the row tiles of one band times a few column tiles. An A
+// row tile is thus shared by about ASHARE column tiles: column tile n takes
+// rows (256 / ASHARE) (n % ASHARE) onwards, 256 / ASHARE of them. A B column
+// tile is shared by the `cnt` row tiles of the band that use the same B
+// (all of the band, or in a grouped GEMM the band's tiles of one group); the
+// row tile at position `idx` among them takes the idx-th of cnt equal
+// slices of its rows.
+template <int ASHARE>
 __device__ __forceinline__ void set_prefetch_shares(TileSpec& ts, int n, int idx, int cnt) {
-  ts.pf_a0 = 64 * (n & 3);
-  ts.pf_an = 64;
+  ts.pf_a0 = (kBM / ASHARE) * (n % ASHARE);
+  ts.pf_an = kBM / ASHARE;
   const int part = (kBM + cnt - 1) / cnt;
   ts.pf_b0 = idx * part;
   ts.pf_bn = part;
@@ -976,9 +990,9 @@ __device__ __forceinline__ int64_t group_start(const int32_t* ends, int g) {
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dense(GemmArgs a) {
   const int mt = (int)((a.M + kBM - 1) / kBM), nt = (int)((a.N + kBN - 1) / kBN);
   int tm, tn, bfirst, brows;
-  const int t = xcd_chunked(blockIdx.x, mt * nt);
+  const int t = xcd_chunked<kOrderDense.chunk>(blockIdx.x, mt * nt);
   if (t < 0) return;
-  band_order(t, mt, nt, tm, tn, bfirst, brows);
+  band_order<kOrderDense.band>(t, mt, nt, tm, tn, bfirst, brows);
   const int64_t m0 = (int64_t)tm * kBM;
   const int64_t n0 = (int64_t)tn * kBN;
   TileSpec ts;
@@ -997,7 +1011,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dense(GemmArgs a) {
   ts.valid_n = (int)min<int64_t>(kBN, a.N - n0);
   ts.k_begin = 0;
   ts.nk = (int)steps;
-  set_prefetch_shares(ts, tn, tm - bfirst, brows);
+  set_prefetch_shares<kOrderDense.a_share>(ts, tn, tm - bfirst, brows);
   const int esz = a.out_f32 ? 4 : 2;
   ts.out = reinterpret_cast<uint8_t*>(a.out) + (m0 * a.ldo + n0) * esz;
   ts.ldo = a.ldo;
@@ -1075,12 +1089,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   const int b = (int)blockIdx.x;
   // the groups' tiles are dealt to the XCDs in chunks; the tail's zero tiles
   // follow the span of that deal, so no XCD's share is padded with them
-  const int span = (int)xcd_chunked_span((int64_t)mt_groups * nt);
+  const int span = (int)xcd_chunked_span<kOrderGrouped.chunk>((int64_t)mt_groups * nt);
   int tile, tn, bfirst, brows;
   if (b < span) {
-    const int t = xcd_chunked(b, mt_groups * nt);
+    const int t = xcd_chunked<kOrderGrouped.chunk>(b, mt_groups * nt);
     if (t < 0) return;
-    band_order(t, mt_groups, nt, tile, tn, bfirst, brows);
+    band_order<kOrderGrouped.band>(t, mt_groups, nt, tile, tn, bfirst, brows);
   } else {
     const int z = b - span;
     if (z >= (mt - mt_groups) * nt) return;
@@ -1136,7 +1150,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   {
     // the band's row tiles that belong to group g share its B tiles
     const int lo = max(bfirst, first), hi = min(bfirst + brows, tile_end[g]);
-    set_prefetch_shares(ts, tn, tile - lo, hi - lo);
+    set_prefetch_shares<kOrderGrouped.a_share>(ts, tn, tile - lo, hi - lo);
   }
   const int esz = a.out_f32 ? 4 : 2;
   ts.out = reinterpret_cast<uint8_t*>(a.out) + (out_row * a.ldo + n0) * esz;
@@ -1179,7 +1193,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_wgrad(GemmArgs a) {
   __syncthreads();
   const int g = pick;
   int tn, tk, bfirst, brows;
-  band_order(u, nt_n, nt_k, tn, tk, bfirst, brows);
+  band_order<kOrderWgrad.band>(u, nt_n, nt_k, tn, tk, bfirst, brows);
   const int64_t ts0 = group_start(ends, g);
   const int64_t n0 = (int64_t)tn * kBM;   // rows of dW = rows of A (= N)
   const int64_t k0 = (int64_t)tk * kBN;   // cols of dW = rows of B (= K)
@@ -1206,7 +1220,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_wgrad(GemmArgs a) {
   ts.valid_n = (int)min<int64_t>(kBN, a.K - k0);
   ts.k_begin = ts0;
   ts.nk = (int)((ends[g] - ts0) / (HP ? kHpT : kBK));
-  set_prefetch_shares(ts, tk, tn - bfirst, brows);
+  set_prefetch_shares<kOrderWgrad.a_share>(ts, tk, tn - bfirst, brows);
   const int esz = a.out_f32 ? 4 : 2;
   ts.out = reinterpret_cast<uint8_t*>(a.out) + (g * a.out_group_stride + n0 * a.ldo + k0) * esz;
   ts.ldo = a.ldo;
@@ -1221,7 +1235,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_wgrad(GemmArgs a) {
 
 
 hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s) {
-  const int64_t tiles = xcd_chunked_span(((a.N + kBN - 1) / kBN) * ((a.M + kBM - 1) / kBM));
+  const int64_t tiles = xcd_chunked_span<kOrderDense.chunk>(((a.N + kBN - 1) / kBN) * ((a.M + kBM - 1) / kBM));
   hipLaunchKernelGGL(k_gemm_dense, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -1229,16 +1243,16 @@ hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) {
   // sum over E groups + tail of ceil(rows / 256) with rows multiples of 128
   const int64_t mtiles = a.M / kBM + (a.E + 2) / 2 + 1;
-  // the chunked deal of the groups' tiles spans at most 8 * kXcdChunk - 1
+  // the chunked deal of the groups' tiles spans at most 8 * chunk - 1
   // indices more than the tiles themselves
-  const int64_t tiles = mtiles * ((a.N + kBN - 1) / kBN) + 8 * kXcdChunk;
+  const int64_t tiles = mtiles * ((a.N + kBN - 1) / kBN) + 8 * kOrderGrouped.chunk;
   hipLaunchKernelGGL(k_gemm_grouped<false>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_grouped_swiglu(const GemmArgs& a, hipStream_t s) {
   const int64_t mtiles = a.M / kBM + (a.E + 2) / 2 + 1;
-  const int64_t tiles = mtiles * (a.N / 2 / 128) + 8 * kXcdChunk;
+  const int64_t tiles = mtiles * (a.N / 2 / 128) + 8 * kOrderGrouped.chunk;
   hipLaunchKernelGGL(k_gemm_grouped<true>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a);
   return hipGetLastError();
 }
