@@ -63,15 +63,17 @@ constexpr int kStageS = (kBM + kBN) * 4;                 // scale dwords of A an
 constexpr int kStageBytes = kStageA + kStageB + kStageS;
 // Tile order per kernel: row tiles per band, tiles per XCD chunk (dense and
 // grouped) and column tiles sharing an A row tile's L2 prefetch. Chosen by
-// paired runs on MI355X over band heights 1-16 and chunks 16-64: against
-// bands of 8 and chunks of 32, the MoE Scout step took 2.8% less time, the
-// dense and DeepSeek-V3-like steps 0.4-1%.
+// paired runs on MI355X over band heights 1-16 and chunks 8-64: against one
+// order for all (bands of 8, chunks of 32), the MoE Scout step took about
+// 2.5% less time, the dense and DeepSeek-V3-like steps 0.4-1%. The weight
+// gradient does best with bands of 3 or 6 rather than 4 or 5 (about 3% on
+// MoE Scout, 1% on the DeepSeek-V3-like shapes, both recipes).
 struct TileOrder {
   int band, chunk, a_share;
 };
 constexpr TileOrder kOrderDense{4, 16, 4};
 constexpr TileOrder kOrderGrouped{2, 16, 8};
-constexpr TileOrder kOrderWgrad{4, 0, 4};
+constexpr TileOrder kOrderWgrad{3, 0, 4};
 constexpr int kMaxGroups = 1024;                         // group table lives in LDS
 #ifndef MX_GEMM_PREFETCH
 #define MX_GEMM_PREFETCH 1
