@@ -1,0 +1,115 @@
+"""Expert counts past one wavefront: the kernels build their group tables 64
+groups at a time (prefix sums carried across passes), up to the ABI's 1024.
+With 200 and 1024 ragged groups, many of them empty, every grouped entry
+point is checked against the oracle bit for bit: the operands are small
+integers under power-of-two scales, which the MFMA sums exactly (and the
+bf16 wgrad_with_hp sums exactly in float32 before its one rounding)."""
+
+import numpy as np
+import pytest
+import torch
+
+from _helpers import bf16_host, dev, host, k128, plain, to_dev
+from oracle import mx as O
+from quantize_grouped_gemm_amd import mx, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _int_mx(shape, seed):
+    """Codes of 0, +-1 .. +-8 and scale bytes 127..130: exact MFMA sums."""
+    rng = np.random.default_rng(seed)
+    vals = np.array([0, 1, 2, 3, 4, 6, 8, -1, -2, -3, -4, -6, -8], np.float64)
+    q = O.e4m3_encode(rng.choice(vals, shape))
+    s = rng.integers(127, 131, shape[:-1] + (shape[-1] // 32,)).astype(np.uint8)
+    return q, s
+
+
+def _mx_dev(q, s):
+    return to_dev(q), to_dev(k128(s))
+
+
+def _slots(E, seed, p_empty):
+    """Per-group slots in 128-row units: empty with probability p_empty, else
+    1..3 slots; the last group is forced non-empty."""
+    rng = np.random.default_rng(seed)
+    n = np.where(rng.random(E) < p_empty, 0, rng.integers(1, 4, E))
+    n[-1] = max(n[-1], 1)
+    return (n * 128).astype(np.int64)
+
+
+@pytest.mark.parametrize("E,p_empty", [(200, 0.35), (1024, 0.8)])
+def test_many_groups_fwd_dgrad(gpu, E, p_empty):
+    N, K = 256, 128
+    offs = np.cumsum(_slots(E, E, p_empty)).astype(np.int32)
+    Tcap = int(offs[-1]) + 256
+    qa, sa = _int_mx((Tcap, K), 1)
+    qw, sw = _int_mx((E, N, K), 2)
+    ref = O.grouped_mm(qa, sa, qw, sw, offs)
+    for fn in (mx.grouped_mm_fwd, mx.grouped_mm_dgrad):
+        err = torch.zeros(1, dtype=torch.int32, device=dev())
+        out = torch.full((Tcap, N), float("nan"), dtype=torch.float32, device=dev())
+        got = fn(*_mx_dev(qa, sa), *_mx_dev(qw, sw), to_dev(offs), torch.float32, out=out, dev_err=err)
+        np.testing.assert_array_equal(host(got).astype(np.float64), ref, err_msg=fn.__name__)
+        assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("E", [200, 1024])
+def test_many_groups_token_order_and_pad_quantize(gpu, E):
+    """Routed tokens with ragged sizes (empty experts included): fused pad +
+    quantize against the oracle, then the token-order forward against the
+    oracle's padded result unpadded."""
+    rng = np.random.default_rng(E + 1)
+    sizes = np.where(rng.random(E) < 0.4, 0, rng.integers(1, 200, E)).astype(np.int32)
+    T = int(sizes.sum())
+    Tcap = synth.capacity(T, E)
+    D, N = 128, 256
+    xb = synth.bits(synth.normal_bf16((T, D), 1.0, synth.generator(E)))
+    x = to_dev(xb.view(np.int16)).view(torch.bfloat16)
+    err = torch.zeros(1, dtype=torch.int32, device=dev())
+    got = mx.pad_quantize(x, to_dev(sizes), Tcap, "rceil", True, False, dev_err=err)
+    ref = O.pad_quantize(xb, sizes, 128, Tcap, "rceil", True, False)
+    np.testing.assert_array_equal(host(got["offs"]), ref["offs"])
+    np.testing.assert_array_equal(host(got["src_row"]), ref["src_row"])
+    np.testing.assert_array_equal(host(got["q_row"]), ref["q_row"])
+    np.testing.assert_array_equal(plain(host(got["s_row"])), ref["s_row"])
+    assert int(err.item()) == 0
+    # token-order forward on exact operands: equals the oracle's padded
+    # product with the pad rows and the tail dropped
+    qa, sa = _int_mx((Tcap, D), 3)
+    qw, sw = _int_mx((E, N, D), 4)
+    padded = O.grouped_mm(qa, sa, qw, sw, ref["offs"])
+    src = ref["src_row"]
+    want = np.zeros((T, N))
+    want[src[src >= 0]] = padded[src >= 0]
+    got_t = mx.grouped_mm_fwd_unpad(*_mx_dev(qa, sa), *_mx_dev(qw, sw), got["offs"], to_dev(sizes), T,
+                                    torch.float32, dev_err=err)
+    np.testing.assert_array_equal(host(got_t).astype(np.float64), want)
+    assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("E,p_empty", [(200, 0.35), (1024, 0.8)])
+def test_many_groups_wgrad(gpu, E, p_empty):
+    N, K = 128, 160
+    offs = np.cumsum(_slots(E, E + 2, p_empty)).astype(np.int32)
+    Tcap = int(offs[-1]) + 128
+    qg, sg = _int_mx((N, Tcap), 5)
+    qx, sx = _int_mx((K, Tcap), 6)
+    out = torch.full((E, N, K), float("nan"), dtype=torch.float32, device=dev())
+    got = mx.grouped_mm_wgrad(*_mx_dev(qg, sg), *_mx_dev(qx, sx), to_dev(offs), torch.float32, out=out)
+    np.testing.assert_array_equal(host(got).astype(np.float64), O.grouped_mm_wgrad(qg, sg, qx, sx, offs))
+
+
+def test_many_groups_wgrad_hp(gpu):
+    """bf16 operands that are small integers: the float32 sums are exact, so
+    the one bf16 rounding matches the oracle's."""
+    E, N, K = 200, 96, 128
+    offs = np.cumsum(_slots(E, 9, 0.35)).astype(np.int32)
+    Tcap = int(offs[-1]) + 128
+    rng = np.random.default_rng(7)
+    g = torch.from_numpy(rng.integers(-8, 9, (Tcap, N)).astype(np.float32)).to(torch.bfloat16)
+    x = torch.from_numpy(rng.integers(-8, 9, (Tcap, K)).astype(np.float32)).to(torch.bfloat16)
+    out = torch.full((E, N, K), float("nan"), dtype=torch.bfloat16, device=dev())
+    got = mx.grouped_mm_wgrad_hp(g.to(dev()), x.to(dev()), to_dev(offs), out=out)
+    ref = O.grouped_mm_wgrad_hp(synth.bits(g), synth.bits(x), offs)
+    np.testing.assert_array_equal(bf16_host(got).view(np.uint16), O.f64_to_bf16(ref))
