@@ -78,7 +78,7 @@ constexpr int kMaxGroups = 1024;                         // group table lives in
 #ifndef MX_GEMM_PREFETCH
 #define MX_GEMM_PREFETCH 1
 #endif
-constexpr bool kPrefetch = MX_GEMM_PREFETCH;             // L2 prefetch two steps ahead of the DMA
+constexpr bool kPrefetch = MX_GEMM_PREFETCH;             // L2 prefetch one step ahead of the DMA
 constexpr int kDmaOps = 18;                              // vector-memory ops of one step's DMA per wave
 constexpr int kPfOps = kPrefetch ? 2 : 0;                // and of one step's prefetch
 
@@ -466,7 +466,7 @@ __device__ __forceinline__ void interleave() {
 //      are done, then barrier: `cur` is free and `nxt` is complete for all
 //      waves;
 //   3. the DMA of step ks+2 into `cur` (the last step, once past the end:
-//      it is never read) and the L2 prefetch of step ks+4 are issued while
+//      it is never read) and the L2 prefetch of step ks+3 are issued while
 //      sub-step 1's MFMAs run and step ks+1's sub-step 0 operands and scales
 //      are read from `nxt`. The DMA goes out one instruction per MFMA: the
 //      CU's texture path takes about 16 clocks per 1 KB instruction, so
@@ -487,7 +487,7 @@ __device__ __forceinline__ void step_full(const TileDma& d, int ks, int nk, uint
   wg_barrier();
   __builtin_amdgcn_sched_barrier(0);
   issue_step(d, ks + 2 < nk ? ks + 2 : nk - 1, cur);
-  if constexpr (kPrefetch) prefetch_step(d, ks + 4 < nk ? ks + 4 : nk - 1, sink);
+  if constexpr (kPrefetch) prefetch_step(d, ks + 3 < nk ? ks + 3 : nk - 1, sink);
   mfmas<1>(r.a1, r.b1, r.sva, r.svb, 8 * (lane >> 5), acc);
   load_ops<0>(nxt, r.a0, r.b0, wm, wn, lane);
   load_scales(nxt, r.nsa, r.nsb, wm, wn, lane);
@@ -683,7 +683,10 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& tile, const SwigluOut*
   const int nk = ts.nk;
   const int last = nk - 1;
   // prologue: steps 0 and 1 to LDS, each DMA followed by two prefetch loads
-  // (steps 2 and 3; past the end, the last step stands in)
+  // (steps 2 and 3; past the end, the last step stands in). The first loop
+  // step prefetches step 3 again: the waits count on one prefetch pair
+  // after every DMA. (Prefetching one step ahead of the DMA rather than two
+  // made the grouped GEMM 3% faster on MoE Scout shapes.)
   issue_step(d, 0, st0);
   if constexpr (kPrefetch) prefetch_step(d, 2 < nk ? 2 : last, sink);
   issue_step(d, 1 < nk ? 1 : last, st1);
