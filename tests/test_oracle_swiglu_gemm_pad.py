@@ -69,6 +69,28 @@ def test_swiglu_quant_outputs_layout():
         np.exp2(r["s_row"].astype(float) - 127 - 9), 32, axis=-1))
 
 
+def test_swiglu_quant_values_match_torch():
+    """The bf16 tensors the fused oracle functions quantize, against torch's
+    CPU float64 silu and autograd rounded once to bf16: the gate half is the
+    silu argument, the up half the multiplier, and the backward output is
+    [dA | dB] in that order."""
+    a, b, dh = _ab((64, 96), 4)
+    at = torch.from_numpy(mx.bf16_to_f64(a)).requires_grad_()
+    bt = torch.from_numpy(mx.bf16_to_f64(b)).requires_grad_()
+    h = torch.nn.functional.silu(at) * bt
+    h.backward(torch.from_numpy(mx.bf16_to_f64(dh)))
+    f = mx.swiglu_quant_fwd(a, b, "rceil")
+    np.testing.assert_array_equal(f["h"], mx.f64_to_bf16(h.detach().numpy()))
+    r = mx.swiglu_quant_bwd(dh, a, b, "rceil")
+    want = mx.f64_to_bf16(np.concatenate([at.grad.numpy(), bt.grad.numpy()], axis=-1))
+    np.testing.assert_array_equal(r["dab"], want)
+    # and the codes are those of exactly these bf16 tensors
+    for out, src in ((f, f["h"]), (r, r["dab"])):
+        q = mx.quantize_bf16(src, "rceil", True, True)
+        for k in ("q_row", "s_row", "q_col", "s_col"):
+            np.testing.assert_array_equal(out[k], q[k])
+
+
 # ---------------------------------------------------------------- GEMMs
 
 def _rand_mx(rows, cols, seed, code_max=0x7E, scale_lo=110, scale_hi=140):
