@@ -5,8 +5,9 @@
 //   k_dequant         E4M3 x E8M0 -> float32 / bf16
 //
 // All four share one tile scheme. A 256-thread workgroup owns a 128 x 128
-// tile of bf16 values. Thread t holds 8 chunks of 8 consecutive values (one
-// 16-byte load each): chunk j sits at tile row (t >> 4) + 16 j, columns
+// tile of bf16 values (k_quant_tile: two adjacent ones). Thread t holds 8
+// chunks of 8 consecutive values per tile (one 16-byte load each): chunk j
+// sits at tile row (t >> 4) + 16 j, columns
 // 8 (t & 15) .. 8 (t & 15) + 7, so the 4 lanes of a quad hold one 32-value
 // row block and the block maximum is two DPP quad permutes away.
 // Row-wise quantization is done straight from registers. For column-wise
@@ -60,30 +61,50 @@ __device__ __forceinline__ void tile_store_bf16(const uint4 (&v)[kTileChunks], u
 
 // ---------------------------------------------------------------- quantize
 
-// COL: column-wise output requested (the LDS tile exists only then, so the
-// row-only kernel keeps more workgroups resident). NT: non-temporal loads.
+// One workgroup quantizes two adjacent 128 x 128 tiles of the same 128 rows
+// (columns 256 bx .. 256 bx + 255): each row is read as 512 contiguous bytes
+// and its row-wise codes written as 256, which on MI355X made the step's
+// quantize launches 2.5% and column-only quantization 11% faster than one
+// tile per workgroup, at 3 waves per SIMD instead of 5. Both tiles are
+// loaded first; the column-wise pass reuses one LDS tile for the two halves.
+// COL: column-wise output requested (the LDS tile exists only then).
+// NT: non-temporal loads.
 template <bool COL, bool NT>
 __global__ __launch_bounds__(kTileThreads) void k_quant_tile(QuantArgs a) {
   const int64_t bz = blockIdx.z;
   const int64_t r0 = (int64_t)blockIdx.y * kTR;
-  const int64_t c0 = (int64_t)blockIdx.x * kTC;
   const int rows_valid = (int)min<int64_t>(kTR, a.rows - r0);
-  const int cols_valid = (int)min<int64_t>(kTC, a.cols - c0);
-  uint4 v[kTileChunks];
-  if (a.src_row)
-    tile_load_gather<NT>(v, a.x, a.ld, a.src_row, a.src_rows, r0, c0, rows_valid, cols_valid);
-  else
-    tile_load<NT>(v, a.x + (bz * a.rows + r0) * a.ld + c0, a.ld, rows_valid, cols_valid);
-  if (a.q_row) {
-    TileOut o{a.q_row + bz * a.rows * a.cols, a.s_row + bz * a.rows * (a.cols / kBlock), a.cols, a.rows, a.k128};
-    tile_rowq(v, rows_valid, cols_valid, a.rceil, o, r0, c0);
+  uint4 v[2][kTileChunks];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t c0 = ((int64_t)blockIdx.x * 2 + h) * kTC;
+    const int cols_valid = (int)min<int64_t>(kTC, a.cols - c0);
+    if (a.src_row)
+      tile_load_gather<NT>(v[h], a.x, a.ld, a.src_row, a.src_rows, r0, c0, rows_valid, cols_valid);
+    else
+      tile_load<NT>(v[h], a.x + (bz * a.rows + r0) * a.ld + c0, a.ld, rows_valid, cols_valid);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t c0 = ((int64_t)blockIdx.x * 2 + h) * kTC;
+    const int cols_valid = (int)min<int64_t>(kTC, a.cols - c0);
+    if (a.q_row) {
+      TileOut o{a.q_row + bz * a.rows * a.cols, a.s_row + bz * a.rows * (a.cols / kBlock), a.cols, a.rows, a.k128};
+      tile_rowq(v[h], rows_valid, cols_valid, a.rceil, o, r0, c0);
+    }
   }
   if constexpr (COL) {
     __shared__ uint4 lds[kTR * kTC / 8];
-    tile_to_lds(v, lds);
-    __syncthreads();
-    TileOut o{a.q_col + bz * a.rows * a.cols, a.s_col + bz * a.cols * (a.rows / kBlock), a.rows, a.cols, a.k128};
-    tile_colq(lds, rows_valid, cols_valid, a.rceil, o, r0, c0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t c0 = ((int64_t)blockIdx.x * 2 + h) * kTC;
+      const int cols_valid = (int)min<int64_t>(kTC, a.cols - c0);
+      if (h) __syncthreads();
+      tile_to_lds(v[h], lds);
+      __syncthreads();
+      TileOut o{a.q_col + bz * a.rows * a.cols, a.s_col + bz * a.cols * (a.rows / kBlock), a.rows, a.cols, a.k128};
+      tile_colq(lds, rows_valid, cols_valid, a.rceil, o, r0, c0);
+    }
   }
 }
 
@@ -236,7 +257,7 @@ namespace mxk {
 constexpr int64_t kStreamBytes = (int64_t)1 << 30;
 
 hipError_t launch_quant(const QuantArgs& a, int64_t batch, hipStream_t s) {
-  dim3 grid((unsigned)((a.cols + kTC - 1) / kTC), (unsigned)((a.rows + kTR - 1) / kTR),
+  dim3 grid((unsigned)((a.cols + 2 * kTC - 1) / (2 * kTC)), (unsigned)((a.rows + kTR - 1) / kTR),
             (unsigned)batch);
   const bool nt = batch * a.rows * a.cols * 2 < kStreamBytes;
   if (a.q_col) {
