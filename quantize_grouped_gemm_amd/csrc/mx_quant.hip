@@ -61,23 +61,25 @@ __device__ __forceinline__ void tile_store_bf16(const uint4 (&v)[kTileChunks], u
 
 // ---------------------------------------------------------------- quantize
 
-// One workgroup quantizes two adjacent 128 x 128 tiles of the same 128 rows
-// (columns 256 bx .. 256 bx + 255): each row is read as 512 contiguous bytes
-// and its row-wise codes written as 256, which on MI355X made the step's
-// quantize launches 2.5% and column-only quantization 11% faster than one
-// tile per workgroup, at 3 waves per SIMD instead of 5. Both tiles are
-// loaded first; the column-wise pass reuses one LDS tile for the two halves.
+// TILES (1 or 2) adjacent 128 x 128 tiles of the same 128 rows per
+// workgroup. With two, each row is read as 512 contiguous bytes and its
+// row-wise codes written as 256 (at 3 waves per SIMD instead of 5): on
+// MI355X the 1.3-2.7 GB expert-weight launches took 3-4% less time and
+// column-only quantization of a 448 MiB tensor 11% less, while launches
+// through a row map (padding) or with fewer than 48 one-tile workgroups per
+// CU took 8-27% more. launch_quant picks per launch. Both tiles are loaded
+// before either is quantized; the column-wise pass reuses one LDS tile.
 // COL: column-wise output requested (the LDS tile exists only then).
 // NT: non-temporal loads.
-template <bool COL, bool NT>
+template <bool COL, bool NT, int TILES>
 __global__ __launch_bounds__(kTileThreads) void k_quant_tile(QuantArgs a) {
   const int64_t bz = blockIdx.z;
   const int64_t r0 = (int64_t)blockIdx.y * kTR;
   const int rows_valid = (int)min<int64_t>(kTR, a.rows - r0);
-  uint4 v[2][kTileChunks];
+  uint4 v[TILES][kTileChunks];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int64_t c0 = ((int64_t)blockIdx.x * 2 + h) * kTC;
+  for (int h = 0; h < TILES; ++h) {
+    const int64_t c0 = ((int64_t)blockIdx.x * TILES + h) * kTC;
     const int cols_valid = (int)min<int64_t>(kTC, a.cols - c0);
     if (a.src_row)
       tile_load_gather<NT>(v[h], a.x, a.ld, a.src_row, a.src_rows, r0, c0, rows_valid, cols_valid);
@@ -85,8 +87,8 @@ __global__ __launch_bounds__(kTileThreads) void k_quant_tile(QuantArgs a) {
       tile_load<NT>(v[h], a.x + (bz * a.rows + r0) * a.ld + c0, a.ld, rows_valid, cols_valid);
   }
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int64_t c0 = ((int64_t)blockIdx.x * 2 + h) * kTC;
+  for (int h = 0; h < TILES; ++h) {
+    const int64_t c0 = ((int64_t)blockIdx.x * TILES + h) * kTC;
     const int cols_valid = (int)min<int64_t>(kTC, a.cols - c0);
     if (a.q_row) {
       TileOut o{a.q_row + bz * a.rows * a.cols, a.s_row + bz * a.rows * (a.cols / kBlock), a.cols, a.rows, a.k128};
@@ -96,8 +98,8 @@ __global__ __launch_bounds__(kTileThreads) void k_quant_tile(QuantArgs a) {
   if constexpr (COL) {
     __shared__ uint4 lds[kTR * kTC / 8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t c0 = ((int64_t)blockIdx.x * 2 + h) * kTC;
+    for (int h = 0; h < TILES; ++h) {
+      const int64_t c0 = ((int64_t)blockIdx.x * TILES + h) * kTC;
       const int cols_valid = (int)min<int64_t>(kTC, a.cols - c0);
       if (h) __syncthreads();
       tile_to_lds(v[h], lds);
@@ -256,17 +258,30 @@ namespace mxk {
 // slower, so those keep plain loads.
 constexpr int64_t kStreamBytes = (int64_t)1 << 30;
 
-hipError_t launch_quant(const QuantArgs& a, int64_t batch, hipStream_t s) {
-  dim3 grid((unsigned)((a.cols + 2 * kTC - 1) / (2 * kTC)), (unsigned)((a.rows + kTR - 1) / kTR),
+template <int TILES>
+static void launch_quant_t(const QuantArgs& a, int64_t batch, bool nt, hipStream_t s) {
+  dim3 grid((unsigned)((a.cols + TILES * kTC - 1) / (TILES * kTC)), (unsigned)((a.rows + kTR - 1) / kTR),
             (unsigned)batch);
-  const bool nt = batch * a.rows * a.cols * 2 < kStreamBytes;
   if (a.q_col) {
-    if (nt) hipLaunchKernelGGL((k_quant_tile<true, true>), grid, dim3(kTileThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_quant_tile<true, false>), grid, dim3(kTileThreads), 0, s, a);
+    if (nt) hipLaunchKernelGGL((k_quant_tile<true, true, TILES>), grid, dim3(kTileThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_quant_tile<true, false, TILES>), grid, dim3(kTileThreads), 0, s, a);
   } else {
-    if (nt) hipLaunchKernelGGL((k_quant_tile<false, true>), grid, dim3(kTileThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_quant_tile<false, false>), grid, dim3(kTileThreads), 0, s, a);
+    if (nt) hipLaunchKernelGGL((k_quant_tile<false, true, TILES>), grid, dim3(kTileThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_quant_tile<false, false, TILES>), grid, dim3(kTileThreads), 0, s, a);
   }
+}
+
+// Two tiles per workgroup without a row map once the one-tile grid has at
+// least 48 workgroups per CU (see k_quant_tile).
+constexpr int64_t kPairMinTiles = 48 * 256;
+
+hipError_t launch_quant(const QuantArgs& a, int64_t batch, hipStream_t s) {
+  const bool nt = batch * a.rows * a.cols * 2 < kStreamBytes;
+  const int64_t tiles = ((a.cols + kTC - 1) / kTC) * ((a.rows + kTR - 1) / kTR) * batch;
+  if (!a.src_row && tiles >= kPairMinTiles)
+    launch_quant_t<2>(a, batch, nt, s);
+  else
+    launch_quant_t<1>(a, batch, nt, s);
   return hipGetLastError();
 }
 

@@ -174,6 +174,34 @@ def test_quantize_inputs_over_one_gib(gpu):
         np.testing.assert_array_equal(plain(host(got["s_col"][b]))[cols], s)
 
 
+@pytest.mark.parametrize("cols,layout", [(128 * 127, "k128"), (128 * 126 + 64, "plain")])
+def test_quantize_two_tile_path_odd_and_ragged_columns(gpu, cols, layout):
+    """Inputs with at least 48 tiles per CU and no row map are quantized two
+    adjacent column tiles per workgroup: here an odd number of column tiles
+    (the last pair half out of range) and, in the plain layout, a ragged
+    last tile of 64 columns. Sampled rows (row-wise) and columns
+    (column-wise), the last 200 columns included, against the oracle."""
+    R = 128 * 97
+    assert (R // 128) * (-(-cols // 128)) >= 48 * 256
+    g = synth.generator(cols, dev())
+    x = synth.normal_bf16((R, cols), 1.0, g, dev())
+    got = mx.quantize(x, "rceil", True, True, layout=layout)
+    rng = np.random.default_rng(cols)
+    rows = np.unique(np.append(rng.choice(R, 48, replace=False), [0, R - 1]))
+    ccols = np.unique(np.concatenate([rng.choice(cols, 48, replace=False), np.arange(cols - 200, cols)]))
+    ri = torch.as_tensor(rows, device=dev())
+    ci = torch.as_tensor(ccols, device=dev())
+    s_row, s_col = host(got["s_row"]), host(got["s_col"])
+    if layout == "k128":
+        s_row, s_col = plain(s_row), plain(s_col)
+    q, s = O.quantize(O.bf16_to_f64(bf16_host(x[ri])), "rceil")
+    np.testing.assert_array_equal(host(got["q_row"][ri]), q)
+    np.testing.assert_array_equal(s_row[rows], s)
+    q, s = O.quantize(O.bf16_to_f64(bf16_host(x[:, ci])).T, "rceil")
+    np.testing.assert_array_equal(host(got["q_col"][ci]), q)
+    np.testing.assert_array_equal(s_col[ccols], s)
+
+
 @pytest.mark.parametrize("layout", ["plain", "k128"])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_dequantize_all_codes_all_scales(gpu, out_dtype, layout):
