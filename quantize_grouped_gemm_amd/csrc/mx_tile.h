@@ -168,8 +168,24 @@ __device__ __forceinline__ void tile_colq(const uint4* lds4, int rows_valid, int
 }
 
 
-// 1 / (1 + e^-a) in float32 without a division: t = e^-|a| (the accurate
-// expf) lies in (0, 1], so d = 1 + t lies in (1, 2] and its reciprocal, by
+// e^x for x <= 0 (and for -inf, giving 0, and NaN, giving NaN), within an
+// ulp or two: Cody-Waite reduction with log2(e) split into a float32 head and
+// tail, x log2(e) = k + f with k = rint(x log2(e)) and |f| <= 1/2, then
+// v_exp_f32 (2^f) scaled by 2^k. f = fma(x, head, -k) + x tail: the fused
+// product-difference is rounded once (a compensated form would be undone by
+// the compiler's floating-point contraction). x <= 0 rules out overflow, so
+// the only guard left is underflow: below ln(2^-149) the result is 0.
+__device__ __forceinline__ float exp_nonpos(float x) {
+  constexpr float kLog2eHi = 1.44269502162933349609375f;   // float32(log2 e)
+  constexpr float kLog2eLo = 1.92596303e-08f;              // float32(log2 e - kLog2eHi)
+  const float k = __builtin_rintf(x * kLog2eHi);
+  const float f = fmaf(x, kLog2eHi, -k) + x * kLog2eLo;
+  const float r = ldexpf(__builtin_amdgcn_exp2f(f), (int)k);
+  return x < -103.278929903431851f ? 0.0f : r;
+}
+
+// 1 / (1 + e^-a) in float32 without a division: t = e^-|a| (exp_nonpos)
+// lies in (0, 1], so d = 1 + t lies in (1, 2] and its reciprocal, by
 // v_rcp_f32 refined with one Newton step, is normal and within an ulp of
 // the quotient; sigma(a) = 1/d for a >= 0 and t/d for a < 0. That is 6
 // instructions in place of the 12 of 1 + e^-a and an IEEE division (the
@@ -177,7 +193,7 @@ __device__ __forceinline__ void tile_colq(const uint4* lds4, int rows_valid, int
 // accuracy (under 3 ulp), and sigma keeps e^a's subnormal range where
 // e^-a would overflow. A NaN stays NaN.
 __device__ __forceinline__ float sigmoid_f32(float a) {
-  const float t = expf(-fabsf(a));
+  const float t = exp_nonpos(-fabsf(a));
   const float d = 1.0f + t;
   float r = __builtin_amdgcn_rcpf(d);
   r = fmaf(fmaf(-d, r, 1.0f), r, r);
