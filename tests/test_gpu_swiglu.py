@@ -127,3 +127,44 @@ def test_swiglu_full_size_sampled(gpu, direction):
     qc = host(got["q_col"][torch.as_tensor(col_rows, device=dev())])
     sc = plain(host(got["s_col"][:, torch.as_tensor(col_rows, device=dev())]))
     _assert_close_codes((qc, sc), (ref_c["q_col"], ref_c["s_col"]), "col")
+
+
+def _every_finite_bf16():
+    """All 65536 bf16 bit patterns as a [256, 256] tile, with the 512 Inf and
+    NaN patterns (exponent all ones) replaced by zero."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    bits[(bits & 0x7F80) == 0x7F80] = 0
+    return bits.reshape(256, 256)
+
+
+def _within_one_bf16_ulp(got_bits, ref_bits, what):
+    g, r = O.bf16_to_f64(got_bits), O.bf16_to_f64(ref_bits)
+    ulp = np.exp2(np.maximum(np.floor(np.log2(np.where(r != 0, np.abs(r), 1.0))), -126) - 7)
+    bad = np.abs(g - r) > ulp
+    assert not bad.any(), f"{what}: {int(bad.sum())} values beyond one bf16 ulp, e.g. a bits " \
+                          f"{np.argwhere(bad)[:4].tolist()}"
+
+
+def test_swiglu_every_bf16_gate_value(gpu):
+    """Every finite bf16 gate value a, with b = dh = 1: h = silu(a) and
+    [dA | dB] = [s (1 + a (1 - s)), a s] each within one bf16 ulp of the
+    oracle's correctly rounded value. This covers the sigmoid over its whole
+    range: saturation at both ends, and the gate values near -87 .. -103
+    where e^a is a float32 subnormal while silu(a) is still a bf16 number."""
+    ab = _every_finite_bf16()
+    ones = np.full_like(ab, 0x3F80)
+    zb = np.concatenate([ab, ones], axis=1)
+    z = _dev_bf16(zb)
+    H = ab.shape[1]
+    fwd = mx.swiglu_quant_fwd(z[:, :H], z[:, H:], "rceil", want_h=True, layout="plain")
+    ref = O.swiglu_quant_fwd(ab, ones, "rceil")
+    _within_one_bf16_ulp(bf16_host(fwd["h"]), ref["h"], "h")
+    bwd = mx.swiglu_quant_bwd(_dev_bf16(ones), z[:, :H], z[:, H:], "rceil", want_dab=True, layout="plain")
+    refb = O.swiglu_quant_bwd(ones, ab, ones, "rceil")
+    _within_one_bf16_ulp(bf16_host(bwd["dab"]), refb["dab"], "dA | dB")
+    # the codes: never more than one E4M3 code from the oracle's
+    for got, want in ((fwd, ref), (bwd, refb)):
+        for ax in ("row", "col"):
+            _, nbeyond, _, _ = code_tolerance(host(got["q_" + ax]), host(got["s_" + ax]),
+                                              want["q_" + ax], want["s_" + ax])
+            assert nbeyond == 0, ax
