@@ -461,7 +461,7 @@ def _cpu_baseline():
 def main():
     args = _args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the MXFP8 path here has no multi-GPU mode "
               f"(asked for --gpus {args.gpus}). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
