@@ -15,8 +15,8 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu():
-    """Skip-free GPU fixture: a gpu-marked test must run on a GPU machine; a
-    missing GPU is an error there, not a skip."""
+    """Skip-free GPU fixture: a gpu-marked test needs a GPU and the built
+    library; a missing GPU is an error, not a skip."""
     import torch
     if not torch.cuda.is_available():
         pytest.fail("gpu-marked test needs a GPU")
