@@ -425,7 +425,7 @@ def _vendor_gemm_component(torch, dev, reps=10):
 
 def _cpu_baseline():
     """The oracle on a bounded slice of the default workload: one expert with
-    4096 of its 8192 hidden units and 1024 tokens (about 15 s on 16 host
+    4096 of its 8192 hidden units and 2048 tokens (about 15 s on 16 host
     threads). Weight quantization and the
     token-dependent work are timed separately and each scaled to the full
     step (16 experts x 8192 hidden; 16384 tokens x 8192 hidden)."""
@@ -437,7 +437,7 @@ def _cpu_baseline():
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    E, T, D, Hs = 1, 1024, 5120, 4096
+    E, T, D, Hs = 1, 2048, 5120, 4096
     c = synth.MOE_SCOUT
     x, w1, w3, w2, dy = [synth.bits(t) for t in synth.mlp_inputs(T, D, Hs, E=E, seed=0)]
     w13 = np.concatenate([w1, w3], axis=1)
