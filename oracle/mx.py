@@ -30,11 +30,12 @@ Conventions
 
 Parity status: every function here is pinned by tests/test_oracle_*.py
 against closed forms, exhaustive enumeration, exact rational brute force or an
-independent library routine (torch CPU casts, torch autograd), except the two
-MLP compositions at the bottom, which only chain pinned functions.
-Parity unpinned: dense_mlp_step and moe_mlp_step. They are checked against
-float64 autograd of the unquantized MLP within quantization noise only; the
-pages give no end-to-end value or threshold to pin them to.
+independent library routine (torch CPU casts, torch autograd). The two MLP
+compositions at the bottom chain pinned functions; they are pinned stage by
+stage against a second CPU implementation written with torch primitives
+(torch's float8 casts, float64 matmuls, silu and autograd), each stage fed
+the oracle's own inputs to it, so every operand, axis, scale mode and bf16
+rounding of the wiring is checked (tests/test_oracle_mlp_stages.py).
 """
 
 import numpy as np
@@ -514,8 +515,7 @@ def dense_mlp_step(x, w1, w3, w2, dy, mode, wgrad_dtype="f32"):
 
     x [T, D], w1/w3 [H, D], w2 [D, H], dy [T, D], all bf16 bits.
     w13 = cat(w1, w3) [2H, D] (READING: gate half first).
-    Returns a dict of every stage output. Parity unpinned (a composition of
-    pinned functions; see the module header).
+    Returns a dict of every stage output.
     """
     H = w1.shape[0]
     w13 = np.concatenate([w1, w3], axis=0)
@@ -540,8 +540,7 @@ def moe_mlp_step(x, sizes, w1, w3, w2, dy, mode, Tcap, multiple=128,
 
     x, dy [T, D] bf16 bits in expert-major order; sizes [E] tokens per
     expert; w1/w3 [E, H, D], w2 [E, D, H]. Groups are padded to ``multiple``
-    rows (pad_groups), run through the grouped GEMMs and unpadded. Parity
-    unpinned (a composition of pinned functions; see the module header).
+    rows (pad_groups), run through the grouped GEMMs and unpadded.
     wgrad = "mx" (MXFP8 weight gradients, float ``wgrad_dtype``) or "hp"
     (wgrad_with_hp: bf16 operands, bf16 result).
     recipe = "fp8_rowwise": every operand is quantized with one scale per
