@@ -125,9 +125,12 @@ mx_status mx_quantize(const void* x, int64_t batch, int64_t rows, int64_t cols,
 
 /* Dequantization: out[r, c] = E4M3(q[r, c]) * 2^(scale(r, c/32) - 127),
  * exact in float32 (out_dtype MX_F32) or rounded to nearest-even bf16
- * (MX_BF16). A NaN code or a 0xFF scale gives NaN. q [rows, cols], s in
- * `layout`, out [rows, cols] contiguous; cols % 32 == 0 (% 128 for
- * MX_SCALES_K128). */
+ * (MX_BF16). The pages use MXFP8 values without defining them; this is the
+ * value of an MX element under the OCP MX v1.0 definition above (the
+ * element's E4M3 value times its block's power-of-two scale), i.e. the
+ * inverse the quantization rounds against. A NaN code or a 0xFF scale gives
+ * NaN. q [rows, cols], s in `layout`, out [rows, cols] contiguous;
+ * cols % 32 == 0 (% 128 for MX_SCALES_K128). */
 mx_status mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows,
                         int64_t cols, mx_scale_layout layout,
                         mx_dtype out_dtype, void* out, void* stream);
@@ -169,9 +172,13 @@ mx_status mx_swiglu_quant_bwd(const void* dh, int64_t ld_dh, const void* a,
 
 /* MXFP8 scaled GEMM for the linear override ([P1], Autograd function
  * changes: _to_mxfp8_then_scaled_mm). out[m, n] = sum_k A[m,k] * B[n,k] with
- * A = deq(qa [M, K], sa) and B = deq(qb [N, K], sb), scales in the
- * MX_SCALES_K128 layout (4-byte aligned), float32 accumulation, then
- * rounded to out_dtype (bf16: nearest-even).
+ * A = deq(qa [M, K], sa) and B = deq(qb [N, K], sb), float32 accumulation,
+ * then rounded to out_dtype (bf16: nearest-even).
+ * Every GEMM of this library reads its scales in the MX_SCALES_K128 layout
+ * only (4-byte aligned): a tile's scales for one K step are then one
+ * contiguous run. Scales written in MX_SCALES_PLAIN must be re-quantized (or
+ * permuted) into MX_SCALES_K128 before they are passed to a GEMM; the GEMMs
+ * cannot tell the layouts apart and would read wrong scales.
  * out row stride ld_out elements (>= N). K % 128 == 0; M, N >= 1.
  * The same call serves the forward, the input gradient (A = dY row-wise,
  * B = W column-wise) and the weight gradient (A = dY column-wise, B = X
@@ -196,11 +203,14 @@ mx_status mx_scaled_grouped_mm_fwd(const uint8_t* qa, const uint8_t* sa,
                                    int64_t N, int64_t K, mx_dtype out_dtype,
                                    void* out, int32_t* dev_err, void* stream);
 
-/* MXFP8 grouped GEMM, input gradient: dX_g = dY_g * W_g. Same contraction
- * and argument meaning as the forward with qa = dY [Tcap, N_fwd] quantized
- * along N_fwd (row-wise) and qw = each expert's weight quantized along N_fwd
- * (column-wise of W [E, N_fwd, K_fwd]: [E, K_fwd, N_fwd]); here the call's
- * N is K_fwd and its K is N_fwd. */
+/* MXFP8 grouped GEMM, input gradient: dX_g = dY_g * W_g, the backward of
+ * the grouped_mm override's input ([P1], Tensor subclass changes: the
+ * overrides dispatch to autograd functions wrapping these kernels; [P2],
+ * Autograd func changes: the MXFP8 grouped GEMM autograd function). Same
+ * contraction and argument meaning as the forward with qa = dY [Tcap, N_fwd]
+ * quantized along N_fwd (row-wise) and qw = each expert's weight quantized
+ * along N_fwd (column-wise of W [E, N_fwd, K_fwd]: [E, K_fwd, N_fwd]); here
+ * the call's N is K_fwd and its K is N_fwd. */
 mx_status mx_scaled_grouped_mm_dgrad(const uint8_t* qa, const uint8_t* sa,
                                      const uint8_t* qw, const uint8_t* sw,
                                      const int32_t* offs, int32_t E,
@@ -259,12 +269,20 @@ mx_status mx_scaled_grouped_mm_dgrad_unpad(const uint8_t* qa, const uint8_t* sa,
                                            mx_dtype out_dtype, void* out,
                                            int32_t* dev_err, void* stream);
 
-/* MXFP8 grouped GEMM, weight gradient, 2-D x 2-D: the contraction runs over
- * each group's own tokens. dW[g] = deq(G^T)[:, s_g:e_g] * deq(X^T)[:, s_g:e_g]^T
+/* MXFP8 grouped GEMM, weight gradient, 2-D x 2-D: the backward of the
+ * grouped_mm override's weight ([P1], Tensor subclass changes; [P2],
+ * Autograd func changes: the MXFP8 grouped GEMM autograd function, whose
+ * default recipe computes the weight gradient in MXFP8). The contraction
+ * runs over each group's own tokens:
+ * dW[g] = deq(G^T)[:, s_g:e_g] * deq(X^T)[:, s_g:e_g]^T
  * qg [N, Tcap], sg: dY column-wise (quantized along tokens).
  * qx [K, Tcap], sx: X column-wise. Scales in the MX_SCALES_K128 layout.
  * out [E, N, K] (out_dtype); an empty group's slice is written as zeros.
- * N % 16 == 0, K % 16 == 0, Tcap % 128 == 0. */
+ * N % 16 == 0, K % 16 == 0, Tcap % 128 == 0.
+ * No workspace: every 256 x 256 tile of dW is computed whole by one
+ * workgroup over its group's full token range and written once from
+ * registers (no split of the contraction, so no partial sums to stage);
+ * groups are scheduled largest first to balance the load. */
 mx_status mx_scaled_grouped_mm_wgrad(const uint8_t* qg, const uint8_t* sg,
                                      const uint8_t* qx, const uint8_t* sx,
                                      const int32_t* offs, int32_t E,
@@ -277,7 +295,7 @@ mx_status mx_scaled_grouped_mm_wgrad(const uint8_t* qg, const uint8_t* sg,
  * contraction on the unquantized bf16 operands, float32 accumulation, bf16
  * (nearest-even) result. g [Tcap, N] and x [Tcap, K] bf16 row-major (tokens
  * are the strided axis); out bf16 [E, N, K]. N % 16 == 0, K % 16 == 0,
- * Tcap % 128 == 0. */
+ * Tcap % 128 == 0. No workspace, for the same reason as above. */
 mx_status mx_grouped_mm_wgrad_hp(const void* g, const void* x,
                                  const int32_t* offs, int32_t E, int64_t Tcap,
                                  int64_t N, int64_t K, void* out,
@@ -305,11 +323,16 @@ mx_status mx_quantize_fp8_rowwise(const void* x, int64_t batch, int64_t rows,
  * the rows after offs[E-1] (the weight gradient contracts each group's tokens
  * separately). s [batch, rows/128, cols, 4]. rows % 128 == 0,
  * cols % 128 == 0. work: caller-owned device scratch of batch * (E + 1) *
- * cols int32 (batch * cols without offs), overwritten. Three kernels. */
+ * cols int32 (batch * cols without offs), overwritten. Three kernels.
+ * offs are checked on the device as the grouped GEMMs check theirs
+ * (non-decreasing multiples of 128, at most rows); if they are not and
+ * dev_err is non-NULL, bit 0 of *dev_err is set and the scales are then
+ * unspecified. */
 mx_status mx_quantize_fp8_colwise(const void* x, int64_t batch, int64_t rows,
                                   int64_t cols, int64_t ld,
                                   const int32_t* offs, int32_t E, uint8_t* q,
-                                  uint8_t* s, int32_t* work, void* stream);
+                                  uint8_t* s, int32_t* work, int32_t* dev_err,
+                                  void* stream);
 
 /* Both directions of the same tensor at once: the codes and scales that
  * mx_quantize_fp8_rowwise and mx_quantize_fp8_colwise (with the same offs)
@@ -319,12 +342,13 @@ mx_status mx_quantize_fp8_colwise(const void* x, int64_t batch, int64_t rows,
  * q_col [batch, cols, rows], s_col [batch, rows/128, cols, 4].
  * rows % 128 == 0, cols % 128 == 0. work: caller-owned device scratch of
  * batch * ((E + 1) * cols + rows) int32 (batch * (cols + rows) without
- * offs), overwritten. Three kernels. */
+ * offs), overwritten. Three kernels. offs and dev_err as for
+ * mx_quantize_fp8_colwise. */
 mx_status mx_quantize_fp8_dual(const void* x, int64_t batch, int64_t rows,
                                int64_t cols, int64_t ld, const int32_t* offs,
                                int32_t E, uint8_t* q_row, uint8_t* s_row,
                                uint8_t* q_col, uint8_t* s_col, int32_t* work,
-                               void* stream);
+                               int32_t* dev_err, void* stream);
 
 /* Per-group token padding ([P1], the torchtitan commit adding
  * pad_token_groups_for_grouped_mm; [P3], The integration: pad_multiple=128).
@@ -367,9 +391,13 @@ mx_status mx_pad_quantize(const void* x, const int32_t* group_sizes, int32_t E,
                           int32_t* offs_pad, int32_t* src_row,
                           int32_t* dev_err, void* stream);
 
-/* Inverse of mx_pad_groups: y[src_row[r]] = y_pad[r] for every padded row r
- * with 0 <= src_row[r] < T. y_pad [Tcap, row_bytes], y [T, row_bytes]. Rows
- * of y that no padded row maps to are left untouched. */
+/* Inverse of mx_pad_groups ([P1], the torchtitan commit adding
+ * pad_token_groups_for_grouped_mm: per-group padding kernels for the MXFP8
+ * grouped mm, whose padded results go back to token order; [P3], The
+ * integration: the padded expert-major layout exists for the kernels only):
+ * y[src_row[r]] = y_pad[r] for every padded row r with 0 <= src_row[r] < T.
+ * y_pad [Tcap, row_bytes], y [T, row_bytes]. Rows of y that no padded row
+ * maps to are left untouched. */
 mx_status mx_unpad_groups(const void* y_pad, const int32_t* src_row,
                           int64_t Tcap, int64_t T, int64_t row_bytes, void* y,
                           void* stream);

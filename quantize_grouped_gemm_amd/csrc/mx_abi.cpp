@@ -69,7 +69,7 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 extern "C" {
 
-int mx_abi_version(void) { return 2; }
+int mx_abi_version(void) { return 3; }
 
 const char* mx_last_error(void) { return g_err; }
 
@@ -453,7 +453,7 @@ mx_status mx_quantize_fp8_rowwise(const void* x, int64_t batch, int64_t rows, in
 
 mx_status mx_quantize_fp8_colwise(const void* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
                                   const int32_t* offs, int32_t E, uint8_t* q, uint8_t* s, int32_t* work,
-                                  void* stream) {
+                                  int32_t* dev_err, void* stream) {
   const char* fn = "mx_quantize_fp8_colwise";
   MX_REQUIRE(batch >= 0 && rows >= 0 && cols >= 0, MX_ERR_SHAPE, "%s: negative size", fn);
   MX_REQUIRE(rows % 128 == 0 && cols % 128 == 0, MX_ERR_SHAPE, "%s: rows and cols must be multiples of 128", fn);
@@ -467,12 +467,13 @@ mx_status mx_quantize_fp8_colwise(const void* x, int64_t batch, int64_t rows, in
   MX_DEVICE();
   mxk::Fp8Args a{static_cast<const uint16_t*>(x), batch, rows, cols, ld, q, s, offs, offs ? E : 0,
                  offs ? (int64_t)E + 1 : 1, work};
+  a.dev_err = dev_err;
   return launched(mxk::launch_fp8_colscale(a, as_stream(stream)), fn);
 }
 
 mx_status mx_quantize_fp8_dual(const void* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
                                const int32_t* offs, int32_t E, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
-                               uint8_t* s_col, int32_t* work, void* stream) {
+                               uint8_t* s_col, int32_t* work, int32_t* dev_err, void* stream) {
   const char* fn = "mx_quantize_fp8_dual";
   MX_REQUIRE(batch >= 0 && rows >= 0 && cols >= 0, MX_ERR_SHAPE, "%s: negative size", fn);
   MX_REQUIRE(rows % 128 == 0 && cols % 128 == 0, MX_ERR_SHAPE, "%s: rows and cols must be multiples of 128", fn);
@@ -491,6 +492,7 @@ mx_status mx_quantize_fp8_dual(const void* x, int64_t batch, int64_t rows, int64
   a.q_col = q_col;
   a.s_col = s_col;
   a.row_max = work + batch * segments * cols;
+  a.dev_err = dev_err;
   return launched(mxk::launch_fp8_dual(a, as_stream(stream)), fn);
 }
 

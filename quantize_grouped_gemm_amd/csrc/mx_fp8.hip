@@ -67,11 +67,29 @@ __device__ __forceinline__ int row_segment(const Fp8Args& a, int64_t r) {
 }
 
 // Zeroes the column maxima, and the row maxima that follow them when
-// both directions are asked for.
+// both directions are asked for. Wave 0 of workgroup 0 also checks the
+// segment offsets: non-decreasing multiples of 128 no larger than rows (the
+// grouped GEMMs' rule); otherwise bit 0 of *dev_err is set. Bad offsets only
+// change which segment a tile's scales come from: row_segment's search
+// always returns a segment in [0, E].
 __global__ __launch_bounds__(256) void k_fp8_clear(Fp8Args a) {
   const int64_t n = a.batch * a.segments * a.cols + (a.row_max ? a.batch * a.rows : 0);
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     a.work[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x < 64 && a.offs && a.dev_err) {
+    const int lane = threadIdx.x;
+    bool bad = false;
+    int32_t prev_last = 0;
+    for (int g0 = 0; g0 < a.E; g0 += 64) {
+      const int g = g0 + lane;
+      const int32_t v = g < a.E ? a.offs[g] : INT32_MAX;
+      int32_t prev = __shfl_up(v, 1);
+      if (lane == 0) prev = prev_last;
+      if (g < a.E) bad |= (v & 127) != 0 || v < prev || (int64_t)v > a.rows;
+      prev_last = __shfl(v, 63);
+    }
+    if (__any(bad) && lane == 0) atomicOr(a.dev_err, 1);
+  }
 }
 
 // Column maxima of the tile held in v (tile_load layout, (0,0) at row r0,

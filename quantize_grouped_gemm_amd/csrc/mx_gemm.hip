@@ -75,12 +75,8 @@ constexpr TileOrder kOrderDense{4, 16, 4};
 constexpr TileOrder kOrderGrouped{2, 16, 8};
 constexpr TileOrder kOrderWgrad{3, 0, 4};
 constexpr int kMaxGroups = 1024;                         // group table lives in LDS
-#ifndef MX_GEMM_PREFETCH
-#define MX_GEMM_PREFETCH 1
-#endif
-constexpr bool kPrefetch = MX_GEMM_PREFETCH;             // L2 prefetch one step ahead of the DMA
 constexpr int kDmaOps = 18;                              // vector-memory ops of one step's DMA per wave
-constexpr int kPfOps = kPrefetch ? 2 : 0;                // and of one step's prefetch
+constexpr int kPfOps = 2;                                // and of one step's L2 prefetch
 
 struct TileSpec {
   const uint8_t* a;   // codes of A row 0 of the tile (K index 0)
@@ -487,7 +483,7 @@ __device__ __forceinline__ void step_full(const TileDma& d, int ks, int nk, uint
   wg_barrier();
   __builtin_amdgcn_sched_barrier(0);
   issue_step(d, ks + 2 < nk ? ks + 2 : nk - 1, cur);
-  if constexpr (kPrefetch) prefetch_step(d, ks + 3 < nk ? ks + 3 : nk - 1, sink);
+  prefetch_step(d, ks + 3 < nk ? ks + 3 : nk - 1, sink);
   mfmas<1>(r.a1, r.b1, r.sva, r.svb, 8 * (lane >> 5), acc);
   load_ops<0>(nxt, r.a0, r.b0, wm, wn, lane);
   load_scales(nxt, r.nsa, r.nsb, wm, wn, lane);
@@ -688,9 +684,9 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& tile, const SwigluOut*
   // after every DMA. (Prefetching one step ahead of the DMA rather than two
   // made the grouped GEMM 3% faster on MoE Scout shapes.)
   issue_step(d, 0, st0);
-  if constexpr (kPrefetch) prefetch_step(d, 2 < nk ? 2 : last, sink);
+  prefetch_step(d, 2 < nk ? 2 : last, sink);
   issue_step(d, 1 < nk ? 1 : last, st1);
-  if constexpr (kPrefetch) prefetch_step(d, 3 < nk ? 3 : last, sink);
+  prefetch_step(d, 3 < nk ? 3 : last, sink);
   MX_WAIT_VM_LDS(kDmaOps + 2 * kPfOps);   // step 0 has landed (step 1's DMA and the prefetches may not)
   wg_barrier();
   Regs r;
@@ -746,12 +742,14 @@ struct HpDma {
 // no wait for it before the transposing LDS reads (whose memory operands
 // carry no alias information and would otherwise wait for every DMA in
 // flight). The step loop orders DMA and reads itself: explicit s_waitcnt
-// vmcnt before each workgroup barrier. Nothing else in this kernel uses M0.
+// vmcnt before each workgroup barrier. The statement sets M0, so it names M0
+// as clobbered and the compiler keeps no value of its own there across it.
 __device__ __forceinline__ void dma16(const __amdgpu_buffer_rsrc_t& r, const uint8_t* lds_dst, uint32_t voff,
                                       uint32_t soff) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(const_cast<uint8_t*>(lds_dst));
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(r),
-               "s"(soff));
+               "s"(soff)
+               : "m0");
 }
 
 // DMA of K step ks (64 tokens) of both operands into stage `st` (G part,

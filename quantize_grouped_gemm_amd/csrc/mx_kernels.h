@@ -87,6 +87,7 @@ struct Fp8Args {
   uint8_t* q_col = nullptr;
   uint8_t* s_col = nullptr;
   int32_t* row_max = nullptr;   // [batch, rows], directly after work
+  int32_t* dev_err = nullptr;   // bit 0: bad segment offsets (nullable)
 };
 
 struct PadArgs {

@@ -57,8 +57,8 @@ _SIGS = {
     "mx_pad_quantize": ([_P, _P, _I32, _I64, _I64, _I32, _I64, ctypes.c_int, ctypes.c_uint, ctypes.c_int, _P, _P,
                          _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "mx_quantize_fp8_rowwise": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
-    "mx_quantize_fp8_colwise": ([_P, _I64, _I64, _I64, _I64, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
-    "mx_quantize_fp8_dual": ([_P, _I64, _I64, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "mx_quantize_fp8_colwise": ([_P, _I64, _I64, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
+    "mx_quantize_fp8_dual": ([_P, _I64, _I64, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "mx_unpad_groups": ([_P, _P, _I64, _I64, _I64, _P, _P], ctypes.c_int),
 }
 EXPORTS = tuple(_SIGS)
@@ -137,11 +137,12 @@ def quantize(x, mode="rceil", rowwise=True, colwise=False, layout="k128", out=No
     return out
 
 
-def quantize_fp8(x, rowwise=True, colwise=False, offs=None, out=None, fused=True):
+def quantize_fp8(x, rowwise=True, colwise=False, offs=None, out=None, fused=True, dev_err=None):
     """FP8 with one power-of-two scale per row (column-wise: per column, or
     per column and group with offs). x bf16 [..., R, C]; returns the same
     keys and k128 layouts as quantize(). Both directions go through the
-    one-read-per-pass entry point unless fused=False."""
+    one-read-per-pass entry point unless fused=False. dev_err: optional
+    int32 device flag word for bad offsets."""
     assert x.dtype == torch.bfloat16 and x.stride(-1) == 1
     R, C = x.shape[-2], x.shape[-1]
     lead = tuple(x.shape[:-2])
@@ -161,7 +162,7 @@ def quantize_fp8(x, rowwise=True, colwise=False, offs=None, out=None, fused=True
         work = torch.empty((batch * ((E + 1) * C + R),), dtype=torch.int32, device=dev)
         st = lib().mx_quantize_fp8_dual(_ptr(x), batch, R, C, ld, _ptr(offs), E, _ptr(out["q_row"]),
                                         _ptr(out["s_row"]), _ptr(out["q_col"]), _ptr(out["s_col"]), _ptr(work),
-                                        _stream(dev))
+                                        _ptr(dev_err), _stream(dev))
         _check(st, "mx_quantize_fp8_dual")
         return out
     if rowwise:
@@ -175,7 +176,7 @@ def quantize_fp8(x, rowwise=True, colwise=False, offs=None, out=None, fused=True
         out.setdefault("s_col", _u8(lead + scale_shape(C, R), dev))
         work = torch.empty((batch * (E + 1) * C,), dtype=torch.int32, device=dev)
         st = lib().mx_quantize_fp8_colwise(_ptr(x), batch, R, C, ld, _ptr(offs), E, _ptr(out["q_col"]),
-                                           _ptr(out["s_col"]), _ptr(work), _stream(dev))
+                                           _ptr(out["s_col"]), _ptr(work), _ptr(dev_err), _stream(dev))
         _check(st, "mx_quantize_fp8_colwise")
     return out
 

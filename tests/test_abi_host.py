@@ -34,7 +34,7 @@ def test_header_symbols_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
     assert sorted(mx.EXPORTS) == names
-    assert L.mx_abi_version() == 2
+    assert L.mx_abi_version() == 3
 
 
 def test_argument_errors_are_reported_without_device_work():
@@ -67,11 +67,11 @@ def test_argument_errors_are_reported_without_device_work():
     # FP8 row-scaled: cols not a multiple of 128; column-wise rows not a
     # multiple of 128; offsets without a group count
     assert L.mx_quantize_fp8_rowwise(p, 1, 64, 96, 96, p, p, None) == 2
-    assert L.mx_quantize_fp8_colwise(p, 1, 96, 128, 128, None, 0, p, p, p, None) == 2
-    assert L.mx_quantize_fp8_colwise(p, 1, 128, 128, 128, p, 0, p, p, p, None) == 2
-    assert L.mx_quantize_fp8_dual(p, 1, 96, 128, 128, None, 0, p, p, p, p, p, None) == 2
-    assert L.mx_quantize_fp8_dual(p, 1, 128, 128, 128, p, 0, p, p, p, p, p, None) == 2
-    assert L.mx_quantize_fp8_dual(p, 1, 128, 128, 128, None, 0, p, p, None, p, p, None) == 1
+    assert L.mx_quantize_fp8_colwise(p, 1, 96, 128, 128, None, 0, p, p, p, None, None) == 2
+    assert L.mx_quantize_fp8_colwise(p, 1, 128, 128, 128, p, 0, p, p, p, None, None) == 2
+    assert L.mx_quantize_fp8_dual(p, 1, 96, 128, 128, None, 0, p, p, p, p, p, None, None) == 2
+    assert L.mx_quantize_fp8_dual(p, 1, 128, 128, 128, p, 0, p, p, p, p, p, None, None) == 2
+    assert L.mx_quantize_fp8_dual(p, 1, 128, 128, 128, None, 0, p, p, None, p, p, None, None) == 1
     # fused w13 + SwiGLU: H not a multiple of 128, bad mode
     assert L.mx_scaled_grouped_mm_swiglu_fwd(p, p, p, p, p, 4, 256, 96, 128, 0, p, p, p, p, p, None, None,
                                              None) == 2

@@ -107,3 +107,23 @@ def test_fp8_grouped_gemms_through_the_mx_kernels(gpu):
     for e in (0, 2):
         assert frob_rel(host(dw[e]), ref[e]) <= FROB_MFMA, e
     assert torch.all(dw[1] == 0)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_fp8_bad_offsets_flag_dev_err(gpu, fused):
+    """Segment offsets that are not non-decreasing multiples of 128 within the
+    rows raise bit 0 of dev_err (both the column-wise and the dual entry
+    point); valid ones leave it clear."""
+    b = _inputs((512, 256), 11)
+    x = _bf16_dev(b)
+    for bad in ([128, 100, 512], [256, 128, 384], [128, 256, 640]):
+        err = torch.zeros(1, dtype=torch.int32, device=dev())
+        mx.quantize_fp8(x, rowwise=fused, colwise=True, offs=to_dev(np.array(bad, np.int32)), fused=fused,
+                        dev_err=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) & 1, bad
+    err = torch.zeros(1, dtype=torch.int32, device=dev())
+    mx.quantize_fp8(x, rowwise=fused, colwise=True, offs=to_dev(np.array([128, 128, 384], np.int32)), fused=fused,
+                    dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0

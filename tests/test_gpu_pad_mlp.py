@@ -102,7 +102,9 @@ def test_dense_mlp_step_matches_oracle(gpu):
     w13 = torch.cat([w1, w3]).to(dev())
     net.step(x.to(dev()), w13, w2.to(dev()), dy.to(dev()))
     ref = O.dense_mlp_step(*[synth.bits(t) for t in (x, w1, w3, w2, dy)], "rceil")
-    # z is the first GEMM on bit-exact operands: within 2 bf16 ulp
+    # whole-step comparison by SQNR (each stage is checked against the
+    # oracle on its own inputs in test_gpu_mlp_stages.py); z comes from
+    # bit-exact operands, so it agrees far more closely than the later stages
     assert _sqnr(O.bf16_to_f64(ref["z"]), O.bf16_to_f64(bf16_host(net.z))) > 50
     for k, got in (("y", net.y), ("dh", net.dh), ("dx", net.dx)):
         assert _sqnr(O.bf16_to_f64(ref[k]), O.bf16_to_f64(bf16_host(got))) > 35, k
