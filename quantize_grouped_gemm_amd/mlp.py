@@ -150,6 +150,23 @@ class DenseMLP:
     def gemm_flops(self):
         return 18 * self.T * self.D * self.H
 
+    def gemm_bytes(self):
+        """Algorithmic HBM bytes of each GEMM stage: both MX operands (codes
+        and scales) read once and the output written once."""
+        T, D, H = self.T, self.D, self.H
+        w = self.dw2.element_size()
+        return {"gemm_w13_fwd": _mxb(T, D) + _mxb(2 * H, D) + 2 * T * 2 * H,
+                "gemm_w2_fwd": _mxb(T, H) + _mxb(D, H) + 2 * T * D,
+                "gemm_w2_dgrad": _mxb(T, D) + _mxb(H, D) + 2 * T * H,
+                "gemm_w2_wgrad": _mxb(D, T) + _mxb(H, T) + w * D * H,
+                "gemm_w13_dgrad": _mxb(T, 2 * H) + _mxb(D, 2 * H) + 2 * T * D,
+                "gemm_w13_wgrad": _mxb(2 * H, T) + _mxb(D, T) + w * 2 * H * D}
+
+
+def _mxb(R, C):
+    """Bytes of an MX operand [R, C]: one code per element, one scale per 32."""
+    return R * C * (1 + 1 / 32)
+
 
 class MoEMLP:
     """Buffers and step of the routed-experts MXFP8 SwiGLU MLP: E experts,
@@ -306,7 +323,7 @@ class MoEMLP:
                                         out=dict(x_pad=self.x_pad, offs=self.offs, src_row=self.src),
                                         dev_err=err)),
             Stage("fp8_x", "k_fp8", 0, _qbytes(Tc * D, True) + 2 * Tc * D,
-                  lambda: fq(self.x_pad, True, True, offs=self.offs, out=self.qx)),
+                  lambda: fq(self.x_pad, True, True, offs=self.offs, out=self.qx, dev_err=err)),
             Stage("fp8_w13", "k_fp8", 0, _qbytes(E * 2 * H * D, True) + 2 * E * 2 * H * D,
                   lambda: fq(w13, True, True, out=self.q13)),
             Stage("fp8_w2", "k_fp8", 0, _qbytes(E * D * H, True) + 2 * E * D * H,
@@ -317,7 +334,7 @@ class MoEMLP:
             Stage("swiglu_fwd", "k_swiglu_fwd", 0, Tc * H * (4 + 2 * (1 + 1 / 32) + 2),
                   lambda: mx.swiglu_quant_fwd(z0, z1, m, want_h=True, out=self.hq)),
             Stage("fp8_h", "k_fp8", 0, _qbytes(Tc * H, True) + 2 * Tc * H,
-                  lambda: fq(self.hq["h"], True, True, offs=self.offs, out=self.qh8)),
+                  lambda: fq(self.hq["h"], True, True, offs=self.offs, out=self.qh8, dev_err=err)),
             Stage("gemm_w2_fwd", "k_gemm_grouped", 2 * T * D * H, 0,
                   lambda: mx.grouped_mm_fwd_unpad(self.qh8["q_row"], self.qh8["s_row"], self.q2["q_row"],
                                                   self.q2["s_row"], self.offs, sizes, T, out=self.y, dev_err=err)),
@@ -326,7 +343,7 @@ class MoEMLP:
                                         out=dict(x_pad=self.dy_pad, offs=self.offs2, src_row=self.src2),
                                         dev_err=err)),
             Stage("fp8_dy", "k_fp8", 0, _qbytes(Tc * D, True) + 2 * Tc * D,
-                  lambda: fq(self.dy_pad, True, True, offs=self.offs, out=self.qdy)),
+                  lambda: fq(self.dy_pad, True, True, offs=self.offs, out=self.qdy, dev_err=err)),
             Stage("gemm_w2_dgrad", "k_gemm_grouped", 2 * T * D * H, 0,
                   lambda: mx.grouped_mm_dgrad(self.qdy["q_row"], self.qdy["s_row"], self.q2["q_col"],
                                               self.q2["s_col"], self.offs, out=self.dh, dev_err=err)),
@@ -336,7 +353,7 @@ class MoEMLP:
             Stage("swiglu_bwd", "k_swiglu_bwd", 0, Tc * H * (6 + 4 * (1 + 1 / 32) + 4),
                   lambda: mx.swiglu_quant_bwd(self.dh, z0, z1, m, want_dab=True, out=self.dzq)),
             Stage("fp8_dz", "k_fp8", 0, _qbytes(Tc * 2 * H, True) + 2 * Tc * 2 * H,
-                  lambda: fq(self.dzq["dab"], True, True, offs=self.offs, out=self.qdz8)),
+                  lambda: fq(self.dzq["dab"], True, True, offs=self.offs, out=self.qdz8, dev_err=err)),
             Stage("gemm_w13_dgrad", "k_gemm_grouped", 2 * T * 2 * H * D, 0,
                   lambda: mx.grouped_mm_dgrad_unpad(self.qdz8["q_row"], self.qdz8["s_row"], self.q13["q_col"],
                                                     self.q13["s_col"], self.offs, sizes, T, out=self.dx,
@@ -349,3 +366,20 @@ class MoEMLP:
     def gemm_flops(self):
         """Useful GEMM flops of one step (real tokens only)."""
         return 18 * self.T * self.D * self.H
+
+    def gemm_bytes(self):
+        """Algorithmic HBM bytes of each GEMM stage: operands read once over
+        the padded capacity (the layout the kernels read), all experts'
+        weights, outputs written once (y and dx in token order; every
+        expert's dW, the empty ones as zeros)."""
+        E, T, D, H, Tc = self.E, self.T, self.D, self.H, self.Tcap
+        w = self.dw2.element_size()
+        b = {"gemm_w13_fwd": _mxb(Tc, D) + E * _mxb(2 * H, D) + 2 * Tc * 2 * H,
+             "gemm_w2_fwd": _mxb(Tc, H) + E * _mxb(D, H) + 2 * T * D,
+             "gemm_w2_dgrad": _mxb(Tc, D) + E * _mxb(H, D) + 2 * Tc * H,
+             "gemm_w13_dgrad": _mxb(Tc, 2 * H) + E * _mxb(D, 2 * H) + 2 * T * D,
+             "gemm_w2_wgrad": _mxb(D, Tc) + _mxb(H, Tc) + w * E * D * H,
+             "gemm_w13_wgrad": _mxb(2 * H, Tc) + _mxb(D, Tc) + w * E * 2 * H * D,
+             "gemm_w2_wgrad_hp": 2 * Tc * D + 2 * Tc * H + w * E * D * H,
+             "gemm_w13_wgrad_hp": 2 * Tc * 2 * H + 2 * Tc * D + w * E * 2 * H * D}
+        return b

@@ -28,17 +28,19 @@ def test_padded_ratio_rounds_each_group_up_to_128():
 
 
 class _Stage:
-    def __init__(self, kernel, flops=0.0, nbytes=0.0):
-        self.kernel, self.flops, self.bytes = kernel, flops, nbytes
+    def __init__(self, kernel, flops=0.0, nbytes=0.0, name=""):
+        self.kernel, self.flops, self.bytes, self.name = kernel, flops, nbytes, name
 
 
 def test_kernel_table_and_gemm_roofline():
     # two GEMM launches of 2 and 4 TFLOP taking 1 ms and 2 ms, one 3 GB
-    # bandwidth launch taking 1 ms
-    stages = [_Stage("g", 2e12), _Stage("q", 0.0, 3e9), _Stage("g", 4e12)]
-    out, table = bench._kernel_table(stages, [1e-3, 1e-3, 2e-3])
+    # bandwidth launch taking 1 ms; the second GEMM moves 16 GB (HBM-bound:
+    # 2 ms at 8 TB/s against 0.8 ms of MFMA)
+    stages = [_Stage("g", 2e12, name="a"), _Stage("q", 0.0, 3e9), _Stage("g", 4e12, name="b")]
+    out, table = bench._kernel_table(stages, [1e-3, 1e-3, 2e-3], {"a": 1e9, "b": 16e9})
     assert out["g"] == {"launches_per_step": 2, "ms_per_step": 3.0, "avg_launch_us": 1500.0,
-                        "useful_tflops": 2000.0}
+                        "useful_tflops": 2000.0, "mfma_floor_us": 600.0, "hbm_floor_us": 1062.5,
+                        "roofline_frac": round((0.4e-3 + 2e-3) / 3e-3, 4)}
     assert out["q"]["gbps"] == 3000.0 and "useful_tflops" not in out["q"]
     r = bench._roofline_gemm(table, "g", 5.0e15, traffic=123.0, padded_ratio=1.25,
                              mfma={"mfma_busy": 0.6, "sclk_ghz": 2.0})
