@@ -100,8 +100,10 @@ int mx_abi_version(void);
 /* Message of the last non-OK status returned on the calling thread. */
 const char* mx_last_error(void);
 
-/* Checks that the current HIP device is a gfx950 and loads the kernels.
- * Calling it is optional: every entry point does the same check. */
+/* Checks that the current HIP device is a gfx950, loads the kernels and
+ * looks up the device address of the work area of
+ * mx_quantize_fp8_dual_scratch on it. Calling it is optional: every entry
+ * point does the same check, and that entry point the same look-up. */
 mx_status mx_init(void);
 
 /* MX block quantization ("cast" kernels of [P3], Summary; the operand
@@ -349,6 +351,24 @@ mx_status mx_quantize_fp8_dual(const void* x, int64_t batch, int64_t rows,
                                int32_t E, uint8_t* q_row, uint8_t* s_row,
                                uint8_t* q_col, uint8_t* s_col, int32_t* work,
                                int32_t* dev_err, void* stream);
+
+/* mx_quantize_fp8_dual without the caller's work area, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): same arguments, results and
+ * errors as mx_quantize_fp8_dual, bit for bit, minus `work`. The work area
+ * is the library's own: a 4 MiB device array per GPU (1 Mi int32), held
+ * until the process ends. The call needs batch * ((E + 1) * cols + rows)
+ * int32 of it (batch * (cols + rows) without offs); larger calls are
+ * rejected with MX_ERR_SHAPE before anything is enqueued. It allocates and
+ * frees nothing. Every call on one GPU shares that GPU's array and clears
+ * what it uses first: calls that overlap in time on one GPU (other streams,
+ * other threads) race on it and must be ordered by the caller. */
+mx_status mx_quantize_fp8_dual_scratch(const void* x, int64_t batch,
+                                       int64_t rows, int64_t cols, int64_t ld,
+                                       const int32_t* offs, int32_t E,
+                                       uint8_t* q_row, uint8_t* s_row,
+                                       uint8_t* q_col, uint8_t* s_col,
+                                       int32_t* dev_err, void* stream);
 
 /* Per-group token padding ([P1], the torchtitan commit adding
  * pad_token_groups_for_grouped_mm; [P3], The integration: pad_multiple=128).

@@ -73,7 +73,12 @@ int mx_abi_version(void) { return 3; }
 
 const char* mx_last_error(void) { return g_err; }
 
-mx_status mx_init(void) { return check_device(); }
+mx_status mx_init(void) {
+  mx_status st = check_device();
+  if (st != MX_OK) return st;
+  int32_t* scratch = nullptr;   // set-up of the allocation-free entry point's work area on this device
+  return launched(mxk::fp8_scratch(&scratch), "mx_init");
+}
 
 mx_status mx_quantize(const void* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
                       mx_scale_mode mode, unsigned dirs, mx_scale_layout layout, uint8_t* q_row,
@@ -487,6 +492,38 @@ mx_status mx_quantize_fp8_dual(const void* x, int64_t batch, int64_t rows, int64
              "%s: misaligned pointer", fn);
   MX_DEVICE();
   const int64_t segments = offs ? (int64_t)E + 1 : 1;
+  mxk::Fp8Args a{static_cast<const uint16_t*>(x), batch, rows, cols, ld, q_row, s_row, offs, offs ? E : 0,
+                 segments, work};
+  a.q_col = q_col;
+  a.s_col = s_col;
+  a.row_max = work + batch * segments * cols;
+  a.dev_err = dev_err;
+  return launched(mxk::launch_fp8_dual(a, as_stream(stream)), fn);
+}
+
+mx_status mx_quantize_fp8_dual_scratch(const void* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
+                                       const int32_t* offs, int32_t E, uint8_t* q_row, uint8_t* s_row,
+                                       uint8_t* q_col, uint8_t* s_col, int32_t* dev_err, void* stream) {
+  const char* fn = "mx_quantize_fp8_dual_scratch";
+  MX_REQUIRE(batch >= 0 && rows >= 0 && cols >= 0, MX_ERR_SHAPE, "%s: negative size", fn);
+  MX_REQUIRE(rows % 128 == 0 && cols % 128 == 0, MX_ERR_SHAPE, "%s: rows and cols must be multiples of 128", fn);
+  MX_REQUIRE(ld >= cols && ld % 8 == 0, MX_ERR_ALIGN, "%s: ld must be >= cols and a multiple of 8", fn);
+  MX_REQUIRE(!offs || (E >= 1 && E <= 1024), MX_ERR_SHAPE, "%s: E must be in [1, 1024] with offsets", fn);
+  MX_REQUIRE(rows / 128 <= 65535 && cols / 128 <= 0x7FFFFFFF && batch <= 65535, MX_ERR_SHAPE,
+             "%s: too large for one launch", fn);
+  const int64_t segments = offs ? (int64_t)E + 1 : 1;
+  const int64_t need = batch * (segments * cols + rows);
+  MX_REQUIRE(need <= mxk::kFp8ScratchInts, MX_ERR_SHAPE,
+             "%s: needs %lld int32 of work area, more than the %lld (4 MiB) the library holds; use "
+             "mx_quantize_fp8_dual with a caller workspace", fn, (long long)need, (long long)mxk::kFp8ScratchInts);
+  if (batch == 0 || rows == 0 || cols == 0) return MX_OK;
+  MX_REQUIRE(x && q_row && s_row && q_col && s_col, MX_ERR_NULL, "%s: NULL pointer", fn);
+  MX_REQUIRE(al16(x) && al16(q_row) && al16(q_col) && al4(s_row) && al4(s_col), MX_ERR_ALIGN,
+             "%s: misaligned pointer", fn);
+  MX_DEVICE();
+  int32_t* work = nullptr;
+  mx_status r = launched(mxk::fp8_scratch(&work), fn);
+  if (r != MX_OK) return r;
   mxk::Fp8Args a{static_cast<const uint16_t*>(x), batch, rows, cols, ld, q_row, s_row, offs, offs ? E : 0,
                  segments, work};
   a.q_col = q_col;

@@ -26,8 +26,38 @@
 #include "mx_tile.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace mxk {
+
+// Work area of the allocation-free dual quantizer
+// (mx_quantize_fp8_dual_scratch): a file-scope device array, so the call
+// needs no allocation of its own. Each GPU the library runs on holds its own
+// copy until the process ends. In host code the name is only a stand-in:
+// kernels get the device address that hipGetSymbolAddress returns for the
+// current device (fp8_scratch).
+static __device__ __align__(256) int32_t scratch[kFp8ScratchInts];
+
+namespace {
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[64];   // device address of `scratch`, per device
+}  // namespace
+
+hipError_t fp8_scratch(int32_t** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 constexpr int kRowsPerGroup = 16;   // rows of one k_fp8_rowscale workgroup
 

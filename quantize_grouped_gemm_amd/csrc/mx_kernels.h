@@ -125,6 +125,11 @@ hipError_t launch_pad(const PadArgs& a, hipStream_t s);
 hipError_t launch_fp8_rowscale(const Fp8Args& a, hipStream_t s);
 hipError_t launch_fp8_colscale(const Fp8Args& a, hipStream_t s);
 hipError_t launch_fp8_dual(const Fp8Args& a, hipStream_t s);
+// The library's own work area for the dual FP8 quantizer (int32 elements):
+// fp8_scratch returns its device address on the current device, looked up
+// once per device.
+constexpr int64_t kFp8ScratchInts = int64_t(1) << 20;   // 4 MiB
+hipError_t fp8_scratch(int32_t** ptr);
 hipError_t launch_pad_map(const PadArgs& a, hipStream_t s);   // offs_pad and src_row only
 hipError_t launch_unpad(const UnpadArgs& a, hipStream_t s);
 

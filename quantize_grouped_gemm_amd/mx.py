@@ -59,6 +59,7 @@ _SIGS = {
     "mx_quantize_fp8_rowwise": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "mx_quantize_fp8_colwise": ([_P, _I64, _I64, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
     "mx_quantize_fp8_dual": ([_P, _I64, _I64, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "mx_quantize_fp8_dual_scratch": ([_P, _I64, _I64, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "mx_unpad_groups": ([_P, _P, _I64, _I64, _I64, _P, _P], ctypes.c_int),
 }
 EXPORTS = tuple(_SIGS)
@@ -178,6 +179,32 @@ def quantize_fp8(x, rowwise=True, colwise=False, offs=None, out=None, fused=True
         st = lib().mx_quantize_fp8_colwise(_ptr(x), batch, R, C, ld, _ptr(offs), E, _ptr(out["q_col"]),
                                            _ptr(out["s_col"]), _ptr(work), _ptr(dev_err), _stream(dev))
         _check(st, "mx_quantize_fp8_colwise")
+    return out
+
+
+def quantize_fp8_dual_scratch(x, offs=None, out=None, dev_err=None):
+    """quantize_fp8(x, True, True, offs) through the allocation-free entry
+    point: the library's own device work area instead of a torch-allocated
+    one (outputs are still allocated here unless given in `out`)."""
+    assert x.dtype == torch.bfloat16 and x.stride(-1) == 1
+    R, C = x.shape[-2], x.shape[-1]
+    lead = tuple(x.shape[:-2])
+    batch = 1
+    for d in lead:
+        batch *= d
+    ld = x.stride(-2)
+    assert batch == 1 or x.stride(-3) == R * ld
+    out = dict(out or {})
+    dev = x.device
+    E = 0 if offs is None else offs.shape[0]
+    out.setdefault("q_row", _u8(lead + (R, C), dev))
+    out.setdefault("s_row", _u8(lead + scale_shape(R, C), dev))
+    out.setdefault("q_col", _u8(lead + (C, R), dev))
+    out.setdefault("s_col", _u8(lead + scale_shape(C, R), dev))
+    st = lib().mx_quantize_fp8_dual_scratch(_ptr(x), batch, R, C, ld, _ptr(offs), E, _ptr(out["q_row"]),
+                                            _ptr(out["s_row"]), _ptr(out["q_col"]), _ptr(out["s_col"]),
+                                            _ptr(dev_err), _stream(dev))
+    _check(st, "mx_quantize_fp8_dual_scratch")
     return out
 
 

@@ -30,7 +30,7 @@ def _declared():
 def test_header_symbols_exported_and_bound():
     L = _lib()
     names = _declared()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
     assert sorted(mx.EXPORTS) == names
