@@ -178,6 +178,31 @@ def test_grouped_token_order_equals_unpadded(gpu, sizes, out_dtype):
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_grouped_wgrad_many_group_sizes_exact(gpu, out_dtype):
+    """Whole 256 x 256 dW tiles (N, K multiples of 256) over 70 groups of 0 to
+    9 token steps: odd and even step counts, one-step groups and empty groups
+    in between, so tiles of every length and the zero tiles of empty groups
+    share one launch. Bit-exact against the oracle on integer operands
+    (float32 output; bf16 output is its round-to-nearest-even)."""
+    rng = np.random.default_rng(17)
+    steps = rng.integers(0, 10, 70)
+    steps[[3, 11, 40]] = 0
+    steps[[5, 6, 7]] = 1
+    offs = _offsets(steps * 128)
+    Tcap = int(offs[-1]) + 256
+    E, N, K = len(steps), 1024, 1024
+    qg, sg = _int_mx((N, Tcap), 21)
+    qx, sx = _int_mx((K, Tcap), 22)
+    out = torch.full((E, N, K), float("nan"), dtype=out_dtype, device=dev())
+    got = mx.grouped_mm_wgrad(*_mx_dev(qg, sg), *_mx_dev(qx, sx), to_dev(offs), out_dtype, out=out)
+    ref = O.grouped_mm_wgrad(qg, sg, qx, sx, offs)
+    if out_dtype == torch.float32:
+        np.testing.assert_array_equal(host(got).astype(np.float64), ref)
+    else:
+        np.testing.assert_array_equal(bf16_host(got), O.f64_to_bf16(ref))
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_grouped_wgrad(gpu, out_dtype):
     E, N, K = 4, 272, 320
     slots = np.array([256, 0, 640, 128])
