@@ -200,47 +200,72 @@ __global__ __launch_bounds__(kTileThreads) void k_swiglu_bwd(SwigluBwdArgs a) {
 // across lanes) and their block's scale byte. Chunk i (kCodes codes) is row
 // i / (cols / kCodes); the quotient comes from a precomputed multiplier
 // (FastDiv, 32-bit) when the chunk count fits 32 bits, from 64-bit
-// division otherwise (IDX64).
+// division otherwise (IDX64). The grid-stride loop takes kUnroll chunks per
+// pass and issues all their loads before converting any, so that several
+// loads per wave are in flight.
+template <bool F32, bool IDX64>
+__device__ __forceinline__ void dequant_load(const DequantArgs& a, FastDiv per_row, int64_t per, int64_t i,
+                                             uint32_t (&w)[F32 ? 1 : 2], uint32_t& sb) {
+  constexpr int kCodes = F32 ? 4 : 8;
+  if constexpr (F32) {
+    w[0] = *reinterpret_cast<const uint32_t*>(a.q + 4 * i);
+  } else {
+    const uint2 c = *reinterpret_cast<const uint2*>(a.q + 8 * i);
+    w[0] = c.x;
+    w[1] = c.y;
+  }
+  int64_t r, cc;
+  if constexpr (IDX64) {
+    r = i / per;
+    cc = i - r * per;
+  } else {
+    const uint32_t rr = fdiv((uint32_t)i, per_row);
+    r = rr;
+    cc = (int64_t)((uint32_t)i - rr * per_row.d);
+  }
+  const int64_t blk = (cc * kCodes) >> 5;
+  sb = a.k128 ? a.s[((blk >> 2) * a.rows + r) * 4 + (blk & 3)] : a.s[r * (a.cols / 32) + blk];
+}
+
+template <bool F32>
+__device__ __forceinline__ void dequant_store(const DequantArgs& a, int64_t i, const uint32_t (&w)[F32 ? 1 : 2],
+                                              uint32_t sb) {
+  constexpr int kCodes = F32 ? 4 : 8;
+  float f[kCodes];
+#pragma unroll
+  for (int k = 0; k < kCodes; ++k) {
+    const float v = e4m3_value((w[k >> 2] >> (8 * (k & 3))) & 0xFFu);
+    // v has at most 4 significant bits and |v| >= 2^-9, so v * 2^(sb-127)
+    // is exact in float32 down to 2^-136 (a float32 subnormal); only
+    // E = 127 with |v| > 1 overflows, to infinity
+    f[k] = sb == 0xFFu ? __uint_as_float(0x7FC00000u) : ldexpf(v, (int)sb - 127);
+  }
+  if constexpr (F32)
+    reinterpret_cast<float4*>(a.out)[i] = make_float4(f[0], f[1], f[2], f[3]);
+  else
+    reinterpret_cast<uint4*>(a.out)[i] = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                                   pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+}
+
 template <bool F32, bool IDX64>
 __global__ __launch_bounds__(256) void k_dequant(DequantArgs a, FastDiv per_row) {
   constexpr int kCodes = F32 ? 4 : 8;
+  constexpr int kUnroll = 4;
   const int64_t per = a.cols / kCodes;
   const int64_t n = a.rows * per;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-    uint32_t w[kCodes / 4];
-    if constexpr (F32) {
-      w[0] = *reinterpret_cast<const uint32_t*>(a.q + 4 * i);
-    } else {
-      const uint2 c = *reinterpret_cast<const uint2*>(a.q + 8 * i);
-      w[0] = c.x;
-      w[1] = c.y;
-    }
-    int64_t r, cc;
-    if constexpr (IDX64) {
-      r = i / per;
-      cc = i - r * per;
-    } else {
-      const uint32_t rr = fdiv((uint32_t)i, per_row);
-      r = rr;
-      cc = (int64_t)((uint32_t)i - rr * per_row.d);
-    }
-    const int64_t blk = (cc * kCodes) >> 5;
-    const uint32_t sb = a.k128 ? a.s[((blk >> 2) * a.rows + r) * 4 + (blk & 3)] : a.s[r * (a.cols / 32) + blk];
-    float f[kCodes];
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+    uint32_t w[kUnroll][F32 ? 1 : 2], sb[kUnroll];
 #pragma unroll
-    for (int k = 0; k < kCodes; ++k) {
-      const float v = e4m3_value((w[k >> 2] >> (8 * (k & 3))) & 0xFFu);
-      // v has at most 4 significant bits and |v| >= 2^-9, so v * 2^(sb-127)
-      // is exact in float32 down to 2^-136 (a float32 subnormal); only
-      // E = 127 with |v| > 1 overflows, to infinity
-      f[k] = sb == 0xFFu ? __uint_as_float(0x7FC00000u) : ldexpf(v, (int)sb - 127);
-    }
-    if constexpr (F32)
-      reinterpret_cast<float4*>(a.out)[i] = make_float4(f[0], f[1], f[2], f[3]);
-    else
-      reinterpret_cast<uint4*>(a.out)[i] = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                                                     pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+    for (int u = 0; u < kUnroll; ++u) dequant_load<F32, IDX64>(a, per_row, per, i + u * stride, w[u], sb[u]);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) dequant_store<F32>(a, i + u * stride, w[u], sb[u]);
+  }
+  for (; i < n; i += stride) {
+    uint32_t w[F32 ? 1 : 2], sb;
+    dequant_load<F32, IDX64>(a, per_row, per, i, w, sb);
+    dequant_store<F32>(a, i, w, sb);
   }
 }
 
@@ -309,9 +334,10 @@ static hipError_t launch_dequant_t(const DequantArgs& a, hipStream_t s) {
   const int64_t n = a.rows * a.cols / kCodes;
   if (n == 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((n + 255) / 256, 256 * 64);
-  // the grid-stride index stays below n + grid size; 32-bit quotients need
+  // the grid-stride index stays below n + 4 x grid size (the unrolled pass
+  // reads up to three strides ahead, all below n); 32-bit quotients need
   // that below 2^32
-  if (n + blocks * 256 < ((int64_t)1 << 32))
+  if (n + 4 * blocks * 256 < ((int64_t)1 << 32))
     hipLaunchKernelGGL((k_dequant<F32, false>), dim3((unsigned)blocks), dim3(256), 0, s, a,
                        make_fastdiv((uint32_t)(a.cols / kCodes)));
   else
