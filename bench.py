@@ -113,8 +113,9 @@ def _ensure_lib():
     mx.lib()
 
 
-def _build_workload(name, torch, dev):
-    """Returns (net, args, stages, tokens, description, config)."""
+def _build_workload(name, torch, dev, wgrad_dtype=None):
+    """Returns (net, args, stages, tokens, description, config). wgrad_dtype:
+    dW dtype of the MoE weight gradients (float32 unless given)."""
     import numpy as np
     from quantize_grouped_gemm_amd import mlp, synth
     if name.startswith("moe"):
@@ -138,11 +139,13 @@ def _build_workload(name, torch, dev):
         w13 = torch.cat([w1, w3], dim=1)
         del w1, w3
         sizes_d = torch.from_numpy(sizes.astype(np.int32)).to(dev)
-        net = mlp.MoEMLP(E, T, D, H, Tcap, dev, wgrad=wgrad, recipe=recipe)
+        dwt = wgrad_dtype or torch.float32
+        net = mlp.MoEMLP(E, T, D, H, Tcap, dev, wgrad=wgrad, recipe=recipe, wgrad_dtype=dwt)
         args = (x, sizes_d, w13, w2, dy)
         fmt = "FP8 row-scaled" if recipe == "fp8_rowwise" else "MXFP8"
         config = {"workload": f"{name}: {fmt} SwiGLU MoE MLP fwd+bwd, E={E} D={D} H={H} T={T} "
-                              f"(padded to 128, Tcap={Tcap}), wgrad={'bf16 wgrad_with_hp' if wgrad == 'hp' else 'mxfp8'}",
+                              f"(padded to 128, Tcap={Tcap}), wgrad={'bf16 wgrad_with_hp' if wgrad == 'hp' else 'mxfp8'}"
+                              + (", dW bf16" if dwt == torch.bfloat16 else ""),
                   "experts": E, "dim": D, "hidden": H, "tokens": T, "capacity": Tcap,
                   "group_sizes": [int(v) for v in sizes], "scale_mode": "rceil", "description": desc}
         return net, args, net.stages(*args), T, config
@@ -651,6 +654,15 @@ def main():
             comp["moe_scout_fp8_rowwise"] = {"tokens_per_s": round(tok2 / w2_, 1), "ms_per_step": round(w2_ * 1e3, 3),
                                              "kernels": _kernel_table(s2, p2, n2.gemm_bytes())[0],
                                              "workload": c2["workload"]}
+            del n2, a2, s2
+            torch.cuda.empty_cache()
+            # the same step with bf16 dW (half the weight gradients' bytes
+            # written); the headline keeps float32 dW
+            n2, a2, s2, tok2, c2 = _build_workload("moe_scout", torch, dev, wgrad_dtype=torch.bfloat16)
+            w2_, p2 = _time_stages(s2, max(3, args.steps // 2), 2, torch)
+            comp["moe_scout_bf16_dw"] = {"tokens_per_s": round(tok2 / w2_, 1), "ms_per_step": round(w2_ * 1e3, 3),
+                                         "kernels": _kernel_table(s2, p2, n2.gemm_bytes())[0],
+                                         "workload": c2["workload"]}
             del n2, a2, s2
             torch.cuda.empty_cache()
         for other in ("dense", "moe_dsv3", "moe_dsv3_hp"):
