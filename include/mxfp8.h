@@ -280,7 +280,9 @@ mx_status mx_scaled_grouped_mm_dgrad_unpad(const uint8_t* qa, const uint8_t* sa,
  * qg [N, Tcap], sg: dY column-wise (quantized along tokens).
  * qx [K, Tcap], sx: X column-wise. Scales in the MX_SCALES_K128 layout.
  * out [E, N, K] (out_dtype); an empty group's slice is written as zeros.
- * N % 16 == 0, K % 16 == 0, Tcap % 128 == 0.
+ * N % 16 == 0, K % 16 == 0, Tcap % 128 == 0, Tcap < 2^23 (a tile's 256
+ * operand rows of Tcap codes are addressed with 32-bit offsets);
+ * MX_ERR_SHAPE otherwise.
  * No workspace: every 256 x 256 tile of dW is computed whole by one
  * workgroup over its group's full token range and written once from
  * registers (no split of the contraction, so no partial sums to stage);
