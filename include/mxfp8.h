@@ -181,7 +181,8 @@ mx_status mx_swiglu_quant_bwd(const void* dh, int64_t ld_dh, const void* a,
  * contiguous run. Scales written in MX_SCALES_PLAIN must be re-quantized (or
  * permuted) into MX_SCALES_K128 before they are passed to a GEMM; the GEMMs
  * cannot tell the layouts apart and would read wrong scales.
- * out row stride ld_out elements (>= N). K % 128 == 0; M, N >= 1.
+ * out row stride ld_out elements (>= N). K % 128 == 0, K < 2^23 (a tile's
+ * 256 operand rows are addressed with 32-bit offsets); M, N >= 1.
  * The same call serves the forward, the input gradient (A = dY row-wise,
  * B = W column-wise) and the weight gradient (A = dY column-wise, B = X
  * column-wise). */
@@ -197,7 +198,8 @@ mx_status mx_scaled_mm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb,
  * All scales in the MX_SCALES_K128 layout (per expert for sw).
  * offs: device int32 [E] (see the conventions above).
  * out [Tcap, N] (out_dtype): rows of group g are A_g * W_g^T; rows at or past
- * offs[E-1] are written as zeros. K % 128 == 0, N % 16 == 0, Tcap % 128 == 0.
+ * offs[E-1] are written as zeros. K % 128 == 0, K < 2^23, N % 16 == 0,
+ * Tcap % 128 == 0.
  * dev_err: optional device int32 (see the conventions above). */
 mx_status mx_scaled_grouped_mm_fwd(const uint8_t* qa, const uint8_t* sa,
                                    const uint8_t* qw, const uint8_t* sw,
@@ -230,7 +232,8 @@ mx_status mx_scaled_grouped_mm_dgrad(const uint8_t* qa, const uint8_t* sa,
  * [H/128, Tcap, 4], q_col [H, Tcap] with s_col [Tcap/128, H, 4] (K128
  * scales), the same bytes. h_out (bf16 [Tcap, H]) is optional. Rows past
  * offs[E-1] give z = 0 and h = 0. H % 128 == 0, K % 128 == 0,
- * Tcap % 128 == 0. */
+ * Tcap % 128 == 0, (H + 128) * K < 2^31 (a tile's gate and up rows are
+ * addressed with 32-bit offsets). */
 mx_status mx_scaled_grouped_mm_swiglu_fwd(const uint8_t* qa, const uint8_t* sa,
                                           const uint8_t* qw13,
                                           const uint8_t* sw13,

@@ -28,6 +28,8 @@ bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // The GEMMs address a K128 scale matrix with 32-bit buffer offsets.
 bool scales_fit(int64_t rows, int64_t k) { return rows * (k / 32) < (1ll << 31); }
+// A GEMM tile's 256 operand rows of K codes are addressed with 32-bit offsets.
+bool k_fits(int64_t k) { return k * 256 < (1ll << 31); }
 
 // 0 = unknown, 1 = gfx950, -1 = other
 int g_dev_ok[64];
@@ -207,6 +209,7 @@ mx_status mx_scaled_mm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
   MX_REQUIRE((M + 255) / 256 * ((N + 255) / 256) + 4096 <= 0x7FFFFFFF, MX_ERR_SHAPE,
              "%s: too many tiles for one launch", fn);
   MX_REQUIRE(scales_fit(M, K) && scales_fit(N, K), MX_ERR_SHAPE, "%s: scale matrices too large", fn);
+  MX_REQUIRE(k_fits(K), MX_ERR_SHAPE, "%s: K (%lld) must be below 2^23", fn, (long long)K);
   if (M == 0 || N == 0) return MX_OK;
   MX_CHECK(check_mx_operand(fn, "A", qa, sa));
   MX_CHECK(check_mx_operand(fn, "B", qb, sb));
@@ -238,6 +241,7 @@ static mx_status grouped_2d3d(const char* fn, const uint8_t* qa, const uint8_t* 
   MX_REQUIRE((Tcap / 256 + (E + 2) / 2 + 1) * ((N + 255) / 256) + 4096 <= 0x7FFFFFFF, MX_ERR_SHAPE,
              "%s: too many tiles for one launch", fn);
   MX_REQUIRE(scales_fit(Tcap, K) && scales_fit(N, K), MX_ERR_SHAPE, "%s: scale matrices too large", fn);
+  MX_REQUIRE(k_fits(K), MX_ERR_SHAPE, "%s: K (%lld) must be below 2^23", fn, (long long)K);
   if (Tcap == 0) return MX_OK;
   MX_CHECK(check_mx_operand(fn, "A", qa, sa));
   MX_CHECK(check_mx_operand(fn, "W", qw, sw));
@@ -271,6 +275,8 @@ mx_status mx_scaled_grouped_mm_swiglu_fwd(const uint8_t* qa, const uint8_t* sa, 
              "%s: too many tiles for one launch", fn);
   MX_REQUIRE(scales_fit(Tcap, K) && scales_fit(2 * H, K), MX_ERR_SHAPE, "%s: scale matrices too large", fn);
   MX_REQUIRE(Tcap * 2 * H * 2 < (1ll << 40), MX_ERR_SHAPE, "%s: z too large", fn);
+  // a tile's B rows span the gate rows and the up rows H rows further
+  MX_REQUIRE((H + 128) * K < (1ll << 31), MX_ERR_SHAPE, "%s: (H + 128) x K must be below 2^31", fn);
   if (Tcap == 0) return MX_OK;
   MX_CHECK(check_mx_operand(fn, "A", qa, sa));
   MX_CHECK(check_mx_operand(fn, "W13", qw, sw));

@@ -62,6 +62,14 @@ def test_argument_errors_are_reported_without_device_work():
     # grouped: Tcap not a multiple of 128, bad E
     assert L.mx_scaled_grouped_mm_fwd(p, p, p, p, p, 4, 100, 64, 128, 0, p, None, None) == 2
     assert L.mx_scaled_grouped_mm_wgrad(p, p, p, p, p, 0, 128, 64, 64, 1, p, None, None) == 2
+    # GEMM operand rows are addressed with 32-bit offsets: K below 2^23 (and
+    # (H + 128) x K below 2^31 for the fused w13 + SwiGLU)
+    st = L.mx_scaled_mm(p, p, p, p, 256, 256, 1 << 23, 0, p, 256, None)
+    assert st == 2 and b"below 2^23" in L.mx_last_error()
+    assert L.mx_scaled_grouped_mm_fwd(p, p, p, p, p, 4, 256, 64, 1 << 23, 0, p, None, None) == 2
+    st = L.mx_scaled_grouped_mm_swiglu_fwd(p, p, p, p, p, 4, 256, 1 << 16, 1 << 15, 0, p, p, p, p, p, None,
+                                           None, None)
+    assert st == 2 and b"(H + 128)" in L.mx_last_error()
     # MXFP8 weight gradient: 256 rows of Tcap codes must be addressable with 32-bit offsets
     st = L.mx_scaled_grouped_mm_wgrad(p, p, p, p, p, 4, 1 << 23, 16, 16, 1, p, None, None)
     assert st == 2 and b"below 2^23" in L.mx_last_error()
