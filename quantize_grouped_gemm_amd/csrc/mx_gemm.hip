@@ -75,8 +75,10 @@ constexpr TileOrder kOrderDense{4, 16, 4};
 constexpr TileOrder kOrderGrouped{2, 16, 8};
 constexpr TileOrder kOrderWgrad{3, 0, 4};
 constexpr int kMaxGroups = 1024;                         // group table lives in LDS
-constexpr int kDmaOps = 18;                              // vector-memory ops of one step's DMA per wave
-constexpr int kPfOps = 2;                                // and of one step's L2 prefetch
+// vector-memory ops per wave and K step of the MXFP8 loop:
+constexpr int kDmaOpsA = 10;   // A and the scales by DMA
+constexpr int kBLoads = 8;     // B's rows by plain loads (see load_b_regs)
+constexpr int kPfOps = 2;      // the L2 prefetch
 
 struct TileSpec {
   const uint8_t* a;   // codes of A row 0 of the tile (K index 0)
@@ -379,6 +381,8 @@ struct TileDma {
   uint32_t lda, ldb, sstep_a, sstep_b;
   uint32_t k_begin;
   uint32_t brow_add;   // rows added to this wave's B rows (b_hi for the tile's second half)
+  uint32_t voff_rl;    // register B loads: lane offset in a B row block
+  uint32_t lds_wb[2];  // register B writes: lane offset in an 8-row block of the stage (even / odd block)
   int wu;
 };
 
@@ -409,6 +413,56 @@ __device__ __forceinline__ void issue_step(const TileDma& d, int ks, uint8_t* st
                                            kstep * d.sstep_a + 256 * d.wu, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsb, (__attribute__((address_space(3))) void*)(sdst + kBM * 4), 4,
                                            lane4, kstep * d.sstep_b + 4 * (64 * d.wu + d.brow_add), 0, 0);
+}
+
+// The same without the B rows (they come through registers): A's 8
+// instructions and the scale dwords.
+__device__ __forceinline__ void issue_step_a(const TileDma& d, int ks, uint8_t* st) {
+  const uint32_t kb = d.k_begin + (uint32_t)ks * kBK;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t row0 = 64 * d.wu + 8 * i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (__attribute__((address_space(3))) void*)(st + row0 * kBK), 16,
+                                             d.voff_a[i & 1], row0 * d.lda + kb, 0, 0);
+  }
+  uint8_t* sdst = st + kStageA + kStageB + 64 * d.wu * 4;
+  const uint32_t lane4 = (threadIdx.x & 63) * 4;
+  const uint32_t kstep = kb / kBK;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsa, (__attribute__((address_space(3))) void*)sdst, 4, lane4,
+                                           kstep * d.sstep_a + 256 * d.wu, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsb, (__attribute__((address_space(3))) void*)(sdst + kBM * 4), 4,
+                                           lane4, kstep * d.sstep_b + 4 * (64 * d.wu + d.brow_add), 0, 0);
+}
+
+// B rows of K step ks through registers. A stage can be refilled only after
+// the barrier that frees it, and its DMA must have landed by the next
+// barrier; the DMA path takes about 24 clocks per instruction, so with both
+// operands on it a step's 64 instructions per CU filled most of that window.
+// Plain 16-byte loads into registers need no free stage: B's rows are loaded
+// a whole step before they are written to LDS (see step_full), and only A's
+// rows and the scales stay on the DMA. Lane l loads piece l & 7 of row
+// l >> 3 of each of the wave's 8-row blocks (8 lanes read one row's 128
+// bytes) and writes it to slot (l & 7) ^ f(row) = (l & 7) ^ (l >> 3) ^ (i & 1),
+// the layout the DMA produces.
+struct RegB {
+  uint4 v[8];
+};
+
+__device__ __forceinline__ void load_b_regs(const TileDma& d, int ks, RegB& b) {
+  const uint32_t kb = d.k_begin + (uint32_t)ks * kBK;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t row0 = 64 * d.wu + 8 * i;
+    b.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(d.rb, d.voff_rl,
+                                                                             (row0 + d.brow_add) * d.ldb + kb, 0));
+  }
+}
+
+__device__ __forceinline__ void store_b_regs(const TileDma& d, const RegB& b, uint8_t* st) {
+  uint8_t* B = st + kStageA;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint4*>(B + (64 * d.wu + 8 * i) * kBK + d.lds_wb[i & 1]) = b.v[i];
 }
 
 // L2 prefetch of K step ks: one 4-byte load per lane per operand touches
@@ -459,35 +513,58 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
-// One K step ks held in stage buffer `cur`; sub-step 0's
-// operands and the step's scales are in registers. Step ks+1 is in flight to
-// `nxt` (its DMA is followed by exactly two prefetch loads).
-//   1. sub-step 0's MFMAs run while sub-step 1's operands are read from `cur`;
-//   2. wait until this wave's DMA of step ks+1 has landed and its LDS reads
-//      are done, then barrier: `cur` is free and `nxt` is complete for all
-//      waves;
-//   3. the DMA of step ks+2 into `cur` (the last step, once past the end:
-//      it is never read) and the L2 prefetch of step ks+3 are issued while
-//      sub-step 1's MFMAs run and step ks+1's sub-step 0 operands and scales
-//      are read from `nxt`. The DMA goes out one instruction per MFMA: the
-//      CU's texture path takes about 16 clocks per 1 KB instruction, so
-//      issued in a burst the four waves' DMA fills its queue and the
-//      next MFMA waits behind a stalled load.
+// Interleaving of the first half with register B: each of the 16 MFMAs is
+// followed by one LDS read, and by one LDS write (the first 8) or one load
+// (the last 8).
+__device__ __forceinline__ void interleave_rw() {
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (t < 8)
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    else
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+  }
+}
+
+// One K step ks held in stage buffer `cur`; sub-step 0's operands and the
+// step's scales are in registers, step ks+1's B rows are in `rb`, and its A
+// rows and scales are in flight to `nxt` (that DMA is followed by exactly
+// two prefetch loads).
+//   1. sub-step 0's MFMAs run while sub-step 1's operands are read from
+//      `cur`, step ks+1's B rows are written from `rb` to `nxt` (no wave
+//      reads `nxt` before the barrier below, and its DMA fills other rows),
+//      and then step ks+2's B rows are loaded into `rb`, a step ahead of
+//      their LDS writes;
+//   2. wait until this wave's DMA of step ks+1 has landed (only the B loads
+//      just issued and the last prefetch may be outstanding) and its LDS
+//      accesses are done, then barrier: `cur` is free and `nxt` is complete
+//      for all waves;
+//   3. the DMA of step ks+2's A rows and scales into `cur` (the last step,
+//      once past the end: it is never read) and the L2 prefetch of step ks+3
+//      are issued while sub-step 1's MFMAs run and step ks+1's sub-step 0
+//      operands and scales are read from `nxt`. The DMA goes out one
+//      instruction per MFMA: issued in a burst, the four waves' DMA fills
+//      the texture path's queue and the next MFMA waits behind a stalled
+//      load.
 // The MFMA unit thus sees no gap for LDS latency or DMA issue; only the
 // barrier itself lies between the two halves. The last step runs the same
-// code: its DMA rewrites a free buffer and its reads of `nxt` go unused,
-// which keeps a single register assignment for the accumulators.
+// code: its writes and DMA fill a free buffer and its reads of `nxt` go
+// unused, which keeps a single register assignment for the accumulators.
 __device__ __forceinline__ void step_full(const TileDma& d, int ks, int nk, uint8_t* cur, uint8_t* nxt, Regs& r,
-                                          v16f (&acc)[4][4], int wm, int wn, int lane, uint8_t* sink) {
+                                          v16f (&acc)[4][4], int wm, int wn, int lane, uint8_t* sink, RegB& rb) {
   __builtin_amdgcn_sched_barrier(0);
   mfmas<0>(r.a0, r.b0, r.sva, r.svb, 8 * (lane >> 5), acc);
   load_ops<1>(cur, r.a1, r.b1, wm, wn, lane);
-  interleave<1, 0>();
+  store_b_regs(d, rb, nxt);
+  load_b_regs(d, ks + 2 < nk ? ks + 2 : nk - 1, rb);
+  interleave_rw();
   __builtin_amdgcn_sched_barrier(0);
-  MX_WAIT_VM_LDS(kPfOps);
+  MX_WAIT_VM_LDS(kPfOps + kBLoads);
   wg_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  issue_step(d, ks + 2 < nk ? ks + 2 : nk - 1, cur);
+  issue_step_a(d, ks + 2 < nk ? ks + 2 : nk - 1, cur);
   prefetch_step(d, ks + 3 < nk ? ks + 3 : nk - 1, sink);
   mfmas<1>(r.a1, r.b1, r.sva, r.svb, 8 * (lane >> 5), acc);
   load_ops<0>(nxt, r.a0, r.b0, wm, wn, lane);
@@ -668,6 +745,9 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& tile, const SwigluOut*
     d.voff_a[par] = (lane >> 3) * d.lda + 16 * piece;
     d.voff_b[par] = (lane >> 3) * d.ldb + 16 * piece;
   }
+  d.voff_rl = (lane >> 3) * d.ldb + 16 * (lane & 7);
+#pragma unroll
+  for (int par = 0; par < 2; ++par) d.lds_wb[par] = (lane >> 3) * kBK + 16 * ((lane & 7) ^ (lane >> 3) ^ par);
   // the 256 lanes of the workgroup spread over the share's rows
   const uint32_t t = threadIdx.x;
   d.voff_pa = (uint32_t)(ts.pf_a0 + ((t * (uint32_t)ts.pf_an) >> 8)) * d.lda;
@@ -689,11 +769,16 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& tile, const SwigluOut*
   // step prefetches step 3 again: the waits count on one prefetch pair
   // after every DMA. (Prefetching one step ahead of the DMA rather than two
   // made the grouped GEMM 3% faster on MoE Scout shapes.)
+  // Step 0 comes whole by DMA; step 1's B rows are loaded into registers
+  // (the first loop step writes them) and its A rows and scales by DMA.
+  RegB rb;
   issue_step(d, 0, st0);
   prefetch_step(d, 2 < nk ? 2 : last, sink);
-  issue_step(d, 1 < nk ? 1 : last, st1);
+  load_b_regs(d, 1 < nk ? 1 : last, rb);
+  issue_step_a(d, 1 < nk ? 1 : last, st1);
   prefetch_step(d, 3 < nk ? 3 : last, sink);
-  MX_WAIT_VM_LDS(kDmaOps + 2 * kPfOps);   // step 0 has landed (step 1's DMA and the prefetches may not)
+  // step 0 has landed (step 1's loads and DMA and the prefetches may not)
+  MX_WAIT_VM_LDS(2 * kPfOps + kBLoads + kDmaOpsA);
   wg_barrier();
   Regs r;
   load_ops<0>(st0, r.a0, r.b0, wm, wn, lane);
@@ -702,10 +787,10 @@ __device__ __forceinline__ void gemm_tile(const TileSpec& tile, const SwigluOut*
   // has waited for st0's DMA at the barrier before
   int ks = 0;
   for (; ks + 1 < nk; ks += 2) {
-    step_full(d, ks, nk, st0, st1, r, acc, wm, wn, lane, sink);
-    step_full(d, ks + 1, nk, st1, st0, r, acc, wm, wn, lane, sink);
+    step_full(d, ks, nk, st0, st1, r, acc, wm, wn, lane, sink, rb);
+    step_full(d, ks + 1, nk, st1, st0, r, acc, wm, wn, lane, sink, rb);
   }
-  if (ks < nk) step_full(d, ks, nk, st0, st1, r, acc, wm, wn, lane, sink);
+  if (ks < nk) step_full(d, ks, nk, st0, st1, r, acc, wm, wn, lane, sink, rb);
   MX_WAIT_VM_LDS(0);
   finish_tile<FUSED, STREAM>(acc, ts, st0, st1, so, h_r0, h_c0);
 }
