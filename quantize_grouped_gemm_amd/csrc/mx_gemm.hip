@@ -1079,6 +1079,57 @@ __device__ __forceinline__ int64_t group_start(const int32_t* ends, int g) {
   return g == 0 ? 0 : ends[g - 1];
 }
 
+// Fewer than 64 groups: every wave holds the group table in registers,
+// lane g for group g and lane E for the tail. The prefix sums run on DPP
+// moves instead of LDS permutes, and a tile finds its group with one
+// ballot, so no LDS table and no workgroup barrier stand between a
+// workgroup's start and its first DMA.
+constexpr int kWaveGroups = 63;
+
+// Inclusive prefix maximum (MAX) or sum over the wave's 64 lanes of
+// non-negative values: shifts by 1, 2, 4 and 8 within each row of 16
+// lanes, then row 0's last lane into row 1 and row 2's into row 3, then
+// lane 31 into rows 2 and 3. A lane whose source lies outside its row, or
+// that a row mask leaves out, takes 0, which changes neither a maximum nor a
+// sum of non-negative values.
+template <bool MAX>
+__device__ __forceinline__ int32_t wave_scan(int32_t x) {
+  auto step = [&](int32_t y) { x = MAX ? max(x, y) : x + y; };
+  step(__builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false));   // row_shr:1
+  step(__builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false));   // row_shr:2
+  step(__builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false));   // row_shr:4
+  step(__builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false));   // row_shr:8
+  step(__builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false));   // row_bcast:15
+  step(__builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false));   // row_bcast:31
+  return x;
+}
+
+// The value of the lane below (0 for lane 0): DPP wave_shr:1.
+__device__ __forceinline__ int32_t lane_below(int32_t x) {
+  return __builtin_amdgcn_update_dpp(0, x, 0x138, 0xF, 0xF, false);
+}
+
+struct WaveGroups {
+  int32_t end, start;   // lane g < E: group g's rows [start, end); lane E: the tail [ends[E-1], cap)
+};
+
+// The offsets cleaned as load_group_ends cleans them (clamped to [0, cap],
+// rounded down to 128 rows, made non-decreasing), with the same report.
+__device__ __forceinline__ WaveGroups wave_group_ends(const int32_t* offs, int E, int64_t cap, int32_t* dev_err,
+                                                     bool reporter) {
+  const int lane = threadIdx.x & 63;
+  const int32_t raw = lane < E ? offs[lane] : 0;
+  const int32_t c = (int32_t)min<int64_t>(max(raw, 0), cap) & ~127;
+  const bool bad = lane < E && (c != raw || raw < lane_below(raw));
+  const bool any_bad = __any(bad);   // every lane votes
+  if (reporter && threadIdx.x == 0 && any_bad && dev_err) atomicOr(dev_err, 1);
+  const int32_t run = wave_scan<true>(lane < E ? c : 0);
+  WaveGroups w;
+  w.end = lane < E ? run : (lane == E ? (int32_t)cap : 0);
+  w.start = lane_below(w.end);
+  return w;
+}
+
 // ---------------------------------------------------------------- kernels
 
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dense(GemmArgs a) {
@@ -1126,58 +1177,83 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   __shared__ int32_t tile_end[kMaxGroups + 1];   // inclusive prefix of row-tile counts
   __shared__ int32_t tok[kMaxGroups + 1];        // token-order output: first row of each group
   const bool reporter = blockIdx.x == 0;
-  load_group_ends(a.offs, a.E, a.M, ends, a.dev_err, reporter);
-  if (a.sizes && threadIdx.x < 64) {
-    // exclusive prefix of the token counts; a count beyond its group's
-    // padded slot, or a total beyond out_rows, is reported (bit 2)
-    const int lane = threadIdx.x;
-    int32_t carry = 0;
-    bool bad = false;
-    for (int g0 = 0; g0 < a.E; g0 += 64) {
-      const int g = g0 + lane;
-      int32_t n = g < a.E ? a.sizes[g] : 0;
-      if (g < a.E) {
-        const int32_t slot = ends[g] - (int32_t)group_start(ends, g);
-        bad |= n < 0 || n > slot;
-        n = min(max(n, 0), slot);
-      }
-      int32_t v = n;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int32_t o = __shfl_up(v, d);
-        if (lane >= d) v += o;
-      }
-      if (g < a.E) tok[g] = carry + v - n;
-      carry += __shfl(v, 63);
+  const bool small = a.E <= kWaveGroups;
+  // small: lane g of every wave holds group g's rows, its row tiles
+  // [tstart, te) and (token order) its first output row tok; lane E the tail
+  const int lane = threadIdx.x & 63;
+  WaveGroups wg{};
+  int32_t te = 0, tstart = 0, tokv = 0;
+  int mt, mt_groups;   // row tiles: all (the tail's included), the groups'
+  if (small) {
+    wg = wave_group_ends(a.offs, a.E, a.M, a.dev_err, reporter);
+    const int32_t count = lane <= a.E ? (wg.end - wg.start + kBM - 1) / kBM : 0;
+    te = wave_scan<false>(count);
+    tstart = te - count;
+    mt = __builtin_amdgcn_readlane(te, a.E);
+    mt_groups = __builtin_amdgcn_readlane(te, a.E - 1);
+    if (a.sizes) {
+      // exclusive prefix of the token counts, reported as below (bit 2)
+      int32_t n = lane < a.E ? a.sizes[lane] : 0;
+      const int32_t slot = wg.end - wg.start;
+      const bool bad = lane < a.E && (n < 0 || n > slot);
+      n = lane < a.E ? min(max(n, 0), slot) : 0;
+      const int32_t incl = wave_scan<false>(n);
+      tokv = incl - n;   // lane E: the total
+      const bool any_bad = __any(bad) || (int64_t)__builtin_amdgcn_readlane(incl, 63) > a.out_rows;
+      if (reporter && threadIdx.x == 0 && any_bad && a.dev_err) atomicOr(a.dev_err, 4);
     }
-    bad |= (int64_t)carry > a.out_rows;
-    const bool any_bad = __any(bad);   // every lane votes
-    if (lane == 0) tok[a.E] = carry;
-    if (reporter && lane == 0 && any_bad && a.dev_err) atomicOr(a.dev_err, 4);
-  }
-  if (threadIdx.x < 64) {
-    // row-tile counts of groups 0..E (E = the tail), inclusive prefix sum
-    const int lane = threadIdx.x;
-    int32_t carry = 0;
-    for (int g0 = 0; g0 <= a.E; g0 += 64) {
-      const int g = g0 + lane;
-      const int32_t end = g < a.E ? ends[g] : (int32_t)a.M;
-      const int32_t start = g == 0 ? 0 : ends[g - 1];
-      int32_t v = g <= a.E ? (end - start + kBM - 1) / kBM : 0;
+  } else {
+    load_group_ends(a.offs, a.E, a.M, ends, a.dev_err, reporter);
+    if (a.sizes && threadIdx.x < 64) {
+      // exclusive prefix of the token counts; a count beyond its group's
+      // padded slot, or a total beyond out_rows, is reported (bit 2)
+      int32_t carry = 0;
+      bool bad = false;
+      for (int g0 = 0; g0 < a.E; g0 += 64) {
+        const int g = g0 + lane;
+        int32_t n = g < a.E ? a.sizes[g] : 0;
+        if (g < a.E) {
+          const int32_t slot = ends[g] - (int32_t)group_start(ends, g);
+          bad |= n < 0 || n > slot;
+          n = min(max(n, 0), slot);
+        }
+        int32_t v = n;
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        int32_t o = __shfl_up(v, d);
-        if (lane >= d) v += o;
+        for (int d = 1; d < 64; d <<= 1) {
+          const int32_t o = __shfl_up(v, d);
+          if (lane >= d) v += o;
+        }
+        if (g < a.E) tok[g] = carry + v - n;
+        carry += __shfl(v, 63);
       }
-      v += carry;
-      if (g <= a.E) tile_end[g] = v;
-      carry = __shfl(v, 63);
+      bad |= (int64_t)carry > a.out_rows;
+      const bool any_bad = __any(bad);   // every lane votes
+      if (lane == 0) tok[a.E] = carry;
+      if (reporter && lane == 0 && any_bad && a.dev_err) atomicOr(a.dev_err, 4);
     }
-    if (lane == 0) ends[a.E] = (int32_t)a.M;
+    if (threadIdx.x < 64) {
+      // row-tile counts of groups 0..E (E = the tail), inclusive prefix sum
+      int32_t carry = 0;
+      for (int g0 = 0; g0 <= a.E; g0 += 64) {
+        const int g = g0 + lane;
+        const int32_t end = g < a.E ? ends[g] : (int32_t)a.M;
+        const int32_t start = g == 0 ? 0 : ends[g - 1];
+        int32_t v = g <= a.E ? (end - start + kBM - 1) / kBM : 0;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          int32_t o = __shfl_up(v, d);
+          if (lane >= d) v += o;
+        }
+        v += carry;
+        if (g <= a.E) tile_end[g] = v;
+        carry = __shfl(v, 63);
+      }
+      if (lane == 0) ends[a.E] = (int32_t)a.M;
+    }
+    __syncthreads();
+    mt = tile_end[a.E];
+    mt_groups = tile_end[a.E - 1];
   }
-  __syncthreads();
-  const int mt = tile_end[a.E];            // row tiles, the tail's included
-  const int mt_groups = tile_end[a.E - 1]; // row tiles of the groups
   const int64_t H = a.N / 2;   // FUSED: z is [Tcap, 2H]
   const int nt = FUSED ? (int)(H / 128) : (int)((a.N + kBN - 1) / kBN);
   const int b = (int)blockIdx.x;
@@ -1197,15 +1273,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
     bfirst = tile;
     brows = 1;
   }
-  // first group whose row-tile range ends past `tile`
-  int lo = 0, hi = a.E;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (tile_end[mid] > tile) hi = mid; else lo = mid + 1;
+  // the first group whose row-tile range ends past `tile`
+  int g, first, tend;
+  int64_t gs, gend;
+  if (small) {
+    const uint64_t hit = __ballot(lane <= a.E && te > tile);
+    g = hit ? __builtin_ctzll(hit) : a.E;
+    first = __builtin_amdgcn_readlane(tstart, g);
+    tend = __builtin_amdgcn_readlane(te, g);
+    gs = __builtin_amdgcn_readlane(wg.start, g);
+    gend = __builtin_amdgcn_readlane(wg.end, g);
+  } else {
+    int lo = 0, hi = a.E;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (tile_end[mid] > tile) hi = mid; else lo = mid + 1;
+    }
+    g = lo;
+    first = g == 0 ? 0 : tile_end[g - 1];
+    tend = tile_end[g];
+    gs = group_start(ends, g);
+    gend = ends[g];
   }
-  const int g = lo;
-  const int first = g == 0 ? 0 : tile_end[g - 1];
-  const int64_t gs = group_start(ends, g);
   const int64_t m0 = gs + (int64_t)(tile - first) * kBM;
   const int64_t n0 = FUSED ? (int64_t)tn * 128 : (int64_t)tn * kBN;
   TileSpec ts;
@@ -1221,7 +1310,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   ts.sstep_b = 4 * a.srows_b;
   ts.sbytes_a = steps * ts.sstep_a - m0 * 4;
   ts.sbytes_b = steps * ts.sstep_b - n0 * 4;
-  ts.valid_m = (int)min<int64_t>(kBM, ends[g] - m0);
+  ts.valid_m = (int)min<int64_t>(kBM, gend - m0);
   ts.valid_n = FUSED ? kBN : (int)min<int64_t>(kBN, a.N - n0);
   ts.k_begin = 0;
   ts.nk = g < a.E ? (int)(a.K / kBK) : 0;
@@ -1233,9 +1322,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   if (a.sizes) {
     // token order: only the group's real rows, shifted to its token range
     if (g >= a.E) return;                              // no tail rows
+    const int32_t tok0 = small ? __builtin_amdgcn_readlane(tokv, g) : tok[g];
+    const int32_t tok1 = small ? __builtin_amdgcn_readlane(tokv, g + 1) : tok[g + 1];
     const int64_t in_group = m0 - gs;
-    const int64_t real = (int64_t)(tok[g + 1] - tok[g]) - in_group;
-    out_row = tok[g] + in_group;
+    const int64_t real = (int64_t)(tok1 - tok0) - in_group;
+    out_row = tok0 + in_group;
     const int64_t room = a.out_rows - out_row;
     const int64_t rows = min<int64_t>(min<int64_t>(real, room), ts.valid_m);
     if (rows <= 0) return;
@@ -1243,7 +1334,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_grouped(GemmArgs a) {
   }
   {
     // the band's row tiles that belong to group g share its B tiles
-    const int lo = max(bfirst, first), hi = min(bfirst + brows, tile_end[g]);
+    const int lo = max(bfirst, first), hi = min(bfirst + brows, tend);
     set_prefetch_shares<kOrderGrouped.a_share>(ts, tn, tile - lo, hi - lo);
   }
   const int esz = a.out_f32 ? 4 : 2;
@@ -1270,25 +1361,43 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_wgrad(GemmArgs a) {
   const int nt_n = (int)((a.N + kBM - 1) / kBM);
   const int nt_k = (int)((a.K + kBN - 1) / kBN);
   const int per = nt_n * nt_k;
-  const int want = (int)blockIdx.x / per;              // group rank
-  const int u = xcd_remap((int)blockIdx.x - want * per, per);
-  if (threadIdx.x == 0) pick = min(want, a.E - 1);
-  load_group_ends(a.offs, a.E, a.M, ends, a.dev_err, blockIdx.x == 0);   // ends with a barrier
-  // group whose rank (descending size, ties by index) equals `want`
-  for (int g = threadIdx.x; g < a.E; g += blockDim.x) {
-    const int32_t sg = ends[g] - (int32_t)group_start(ends, g);
+  const int want = min((int)blockIdx.x / per, a.E - 1);   // group rank
+  const int u = xcd_remap((int)blockIdx.x - ((int)blockIdx.x / per) * per, per);
+  // the group whose rank (descending size, ties by index) equals `want`
+  int g;
+  int64_t ts0, gend;
+  if (a.E <= kWaveGroups) {
+    const int lane = threadIdx.x & 63;
+    const WaveGroups wg = wave_group_ends(a.offs, a.E, a.M, a.dev_err, blockIdx.x == 0);
+    const int32_t size = wg.end - wg.start;
     int rank = 0;
     for (int h = 0; h < a.E; ++h) {
-      const int32_t sh = ends[h] - (int32_t)group_start(ends, h);
-      rank += (sh > sg) || (sh == sg && h < g);
+      const int32_t sh = __builtin_amdgcn_readlane(size, h);
+      rank += (sh > size) || (sh == size && h < lane);
     }
-    if (rank == want) pick = g;
+    const uint64_t hit = __ballot(lane < a.E && rank == want);
+    g = hit ? __builtin_ctzll(hit) : want;
+    ts0 = __builtin_amdgcn_readlane(wg.start, g);
+    gend = __builtin_amdgcn_readlane(wg.end, g);
+  } else {
+    if (threadIdx.x == 0) pick = want;
+    load_group_ends(a.offs, a.E, a.M, ends, a.dev_err, blockIdx.x == 0);   // ends with a barrier
+    for (int gg = threadIdx.x; gg < a.E; gg += blockDim.x) {
+      const int32_t sg = ends[gg] - (int32_t)group_start(ends, gg);
+      int rank = 0;
+      for (int h = 0; h < a.E; ++h) {
+        const int32_t sh = ends[h] - (int32_t)group_start(ends, h);
+        rank += (sh > sg) || (sh == sg && h < gg);
+      }
+      if (rank == want) pick = gg;
+    }
+    __syncthreads();
+    g = pick;
+    ts0 = group_start(ends, g);
+    gend = ends[g];
   }
-  __syncthreads();
-  const int g = pick;
   int tn, tk, bfirst, brows;
   band_order<kOrderWgrad.band>(u, nt_n, nt_k, tn, tk, bfirst, brows);
-  const int64_t ts0 = group_start(ends, g);
   const int64_t n0 = (int64_t)tn * kBM;   // rows of dW = rows of A (= N)
   const int64_t k0 = (int64_t)tk * kBN;   // cols of dW = rows of B (= K)
   TileSpec ts;
@@ -1313,7 +1422,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_wgrad(GemmArgs a) {
   ts.valid_m = (int)min<int64_t>(kBM, a.N - n0);
   ts.valid_n = (int)min<int64_t>(kBN, a.K - k0);
   ts.k_begin = ts0;
-  ts.nk = (int)((ends[g] - ts0) / (HP ? kHpT : kBK));
+  ts.nk = (int)((gend - ts0) / (HP ? kHpT : kBK));
   set_prefetch_shares<kOrderWgrad.a_share>(ts, tk, tn - bfirst, brows);
   const int esz = a.out_f32 ? 4 : 2;
   ts.out = reinterpret_cast<uint8_t*>(a.out) + (g * a.out_group_stride + n0 * a.ldo + k0) * esz;

@@ -1,9 +1,12 @@
-"""Expert counts past one wavefront: the kernels build their group tables 64
-groups at a time (prefix sums carried across passes), up to the ABI's 1024.
-With 200 and 1024 ragged groups, many of them empty, every grouped entry
-point is checked against the oracle bit for bit: the operands are small
-integers under power-of-two scales, which the MFMA sums exactly (and the
-bf16 wgrad_with_hp sums exactly in float32 before its one rounding)."""
+"""Expert counts on both sides of one wavefront. Below 64 groups the GEMM
+kernels hold the group table in every wave's registers (lane g for group g,
+lane E for the tail; prefix sums by DPP, which crosses 16-lane rows at
+lanes 16, 32 and 48); from 64 on they build it in LDS 64 groups at a time
+(prefix sums carried across passes), up to the ABI's 1024. With 1 to 1024
+ragged groups, many of them empty, every grouped entry point is checked
+against the oracle bit for bit: the operands are small integers under
+power-of-two scales, which the MFMA sums exactly (and the bf16
+wgrad_with_hp sums exactly in float32 before its one rounding)."""
 
 import numpy as np
 import pytest
@@ -38,7 +41,8 @@ def _slots(E, seed, p_empty):
     return (n * 128).astype(np.int64)
 
 
-@pytest.mark.parametrize("E,p_empty", [(200, 0.35), (1024, 0.8)])
+@pytest.mark.parametrize("E,p_empty", [(1, 0.0), (17, 0.35), (33, 0.35), (63, 0.35), (64, 0.35), (200, 0.35),
+                                       (1024, 0.8)])
 def test_many_groups_fwd_dgrad(gpu, E, p_empty):
     N, K = 256, 128
     offs = np.cumsum(_slots(E, E, p_empty)).astype(np.int32)
@@ -54,7 +58,7 @@ def test_many_groups_fwd_dgrad(gpu, E, p_empty):
         assert int(err.item()) == 0
 
 
-@pytest.mark.parametrize("E", [200, 1024])
+@pytest.mark.parametrize("E", [17, 63, 64, 200, 1024])
 def test_many_groups_token_order_and_pad_quantize(gpu, E):
     """Routed tokens with ragged sizes (empty experts included): fused pad +
     quantize against the oracle, then the token-order forward against the
@@ -88,7 +92,8 @@ def test_many_groups_token_order_and_pad_quantize(gpu, E):
     assert int(err.item()) == 0
 
 
-@pytest.mark.parametrize("E,p_empty", [(200, 0.35), (1024, 0.8)])
+@pytest.mark.parametrize("E,p_empty", [(1, 0.0), (17, 0.35), (33, 0.35), (63, 0.35), (64, 0.35), (200, 0.35),
+                                       (1024, 0.8)])
 def test_many_groups_wgrad(gpu, E, p_empty):
     N, K = 128, 160
     offs = np.cumsum(_slots(E, E + 2, p_empty)).astype(np.int32)
@@ -100,10 +105,11 @@ def test_many_groups_wgrad(gpu, E, p_empty):
     np.testing.assert_array_equal(host(got).astype(np.float64), O.grouped_mm_wgrad(qg, sg, qx, sx, offs))
 
 
-def test_many_groups_wgrad_hp(gpu):
+@pytest.mark.parametrize("E", [63, 64, 200])
+def test_many_groups_wgrad_hp(gpu, E):
     """bf16 operands that are small integers: the float32 sums are exact, so
     the one bf16 rounding matches the oracle's."""
-    E, N, K = 200, 96, 128
+    N, K = 96, 128
     offs = np.cumsum(_slots(E, 9, 0.35)).astype(np.int32)
     Tcap = int(offs[-1]) + 128
     rng = np.random.default_rng(7)
@@ -113,3 +119,32 @@ def test_many_groups_wgrad_hp(gpu):
     got = mx.grouped_mm_wgrad_hp(g.to(dev()), x.to(dev()), to_dev(offs), out=out)
     ref = O.grouped_mm_wgrad_hp(synth.bits(g), synth.bits(x), offs)
     np.testing.assert_array_equal(bf16_host(got).view(np.uint16), O.f64_to_bf16(ref))
+
+
+@pytest.mark.parametrize("E", [3, 63, 64, 70])
+def test_bad_offsets_flag_dev_err_both_tables(gpu, E):
+    """Offsets that are not multiples of 128, that decrease, or that pass
+    Tcap raise bit 0 of dev_err in the forward and the weight gradient, with
+    the table in registers (E < 64) and in LDS; valid ones raise nothing."""
+    N, K = 128, 128
+    good = np.cumsum(_slots(E, E + 5, 0.3)).astype(np.int32)
+    Tcap = int(good[-1]) + 128
+    qa, sa = _int_mx((Tcap, K), 11)
+    qw, sw = _int_mx((E, N, K), 12)
+    qg, sg = _int_mx((N, Tcap), 13)
+    qx, sx = _int_mx((K, Tcap), 14)
+    bads = []
+    b = good.copy(); b[E // 2] += 64; bads.append(b)                              # not a multiple of 128
+    if E > 1:
+        b = good.copy(); b[E - 2] = b[E - 1] + 128; bads.append(b)                 # decreasing
+    b = good.copy(); b[-1] = Tcap + 128; bads.append(b)                            # past Tcap
+    for offs in [good] + bads:
+        want = 0 if offs is good else 1
+        for run in ("fwd", "wgrad"):
+            err = torch.zeros(1, dtype=torch.int32, device=dev())
+            if run == "fwd":
+                mx.grouped_mm_fwd(*_mx_dev(qa, sa), *_mx_dev(qw, sw), to_dev(offs), torch.float32, dev_err=err)
+            else:
+                mx.grouped_mm_wgrad(*_mx_dev(qg, sg), *_mx_dev(qx, sx), to_dev(offs), torch.float32, dev_err=err)
+            torch.cuda.synchronize()
+            assert (int(err.item()) & 1) == want, (run, offs.tolist())
