@@ -131,20 +131,21 @@ class DenseMLP:
                                        self.q2["s_row"], out=self.y)),
             Stage("quant_dy", "k_quant_tile", 0, _qbytes(T * D, True),
                   lambda: mx.quantize(dy, m, True, True, out=self.qdy)),
+            # backward in the order described at _stages of MoEMLP
             Stage("gemm_w2_dgrad", "k_gemm_dense", 2 * T * D * H, 0,
                   lambda: mx.scaled_mm(self.qdy["q_row"], self.qdy["s_row"], self.q2["q_col"],
                                        self.q2["s_col"], out=self.dh)),
+            Stage("swiglu_bwd", "k_swiglu_bwd", 0, T * H * (6 + 4 * (1 + 1 / 32)),
+                  lambda: mx.swiglu_quant_bwd(self.dh, z0, z1, m, out=self.dzq)),
             Stage("gemm_w2_wgrad", "k_gemm_dense", 2 * T * D * H, 0,
                   lambda: mx.scaled_mm(self.qdy["q_col"], self.qdy["s_col"], self.hq["q_col"],
                                        self.hq["s_col"], out=self.dw2)),
-            Stage("swiglu_bwd", "k_swiglu_bwd", 0, T * H * (6 + 4 * (1 + 1 / 32)),
-                  lambda: mx.swiglu_quant_bwd(self.dh, z0, z1, m, out=self.dzq)),
-            Stage("gemm_w13_dgrad", "k_gemm_dense", 2 * T * 2 * H * D, 0,
-                  lambda: mx.scaled_mm(self.dzq["q_row"], self.dzq["s_row"], self.q13["q_col"],
-                                       self.q13["s_col"], out=self.dx)),
             Stage("gemm_w13_wgrad", "k_gemm_dense", 2 * T * 2 * H * D, 0,
                   lambda: mx.scaled_mm(self.dzq["q_col"], self.dzq["s_col"], self.qx["q_col"],
                                        self.qx["s_col"], out=self.dw13)),
+            Stage("gemm_w13_dgrad", "k_gemm_dense", 2 * T * 2 * H * D, 0,
+                  lambda: mx.scaled_mm(self.dzq["q_row"], self.dzq["s_row"], self.q13["q_col"],
+                                       self.q13["s_col"], out=self.dx)),
         ]
 
     def gemm_flops(self):
@@ -275,37 +276,40 @@ class MoEMLP:
                                                dev_err=err)),
                    Stage("quant_dy", "k_quant_tile", 0, _qbytes(Tc * D, False),
                          lambda: mx.quantize(self.dy_pad, m, True, False, out=self.qdy))]
+        # Backward: w2 dgrad, the SwiGLU backward, both weight gradients, and
+        # the w13 dgrad last. Each weight gradient writes its whole dW, and the
+        # kernel after it pays for writing back those lines from the caches:
+        # a GEMM hides that under its arithmetic, a bandwidth-bound kernel (the
+        # SwiGLU backward, or the next step's weight quantization) does not.
         st += [
             Stage("gemm_w2_dgrad", "k_gemm_grouped", 2 * T * D * H, 0,
                   lambda: mx.grouped_mm_dgrad(self.qdy["q_row"], self.qdy["s_row"], self.q2["q_col"],
                                               self.q2["s_col"], self.offs, out=self.dh, dev_err=err)),
-        ]
-        if mxw:
-            st.append(Stage("gemm_w2_wgrad", "k_gemm_wgrad", 2 * T * D * H, 0,
-                            lambda: mx.grouped_mm_wgrad(self.qdy["q_col"], self.qdy["s_col"], self.hq["q_col"],
-                                                        self.hq["s_col"], self.offs, out=self.dw2,
-                                                        dev_err=err)))
-        else:
-            st.append(Stage("gemm_w2_wgrad_hp", "k_gemm_wgrad_hp", 2 * T * D * H, 0,
-                            lambda: mx.grouped_mm_wgrad_hp(self.dy_pad, self.hq["h"], self.offs, out=self.dw2,
-                                                           dev_err=err)))
-        st += [
             Stage("swiglu_bwd", "k_swiglu_bwd", 0, Tc * H * (6 + 4 * (1 + 1 / 32) + (0 if mxw else 4)),
                   lambda: mx.swiglu_quant_bwd(self.dh, z0, z1, m, want_dab=not mxw, out=self.dzq)),
-            Stage("gemm_w13_dgrad", "k_gemm_grouped", 2 * T * 2 * H * D, 0,
-                  lambda: mx.grouped_mm_dgrad_unpad(self.dzq["q_row"], self.dzq["s_row"], self.q13["q_col"],
-                                                    self.q13["s_col"], self.offs, sizes, T, out=self.dx,
-                                                    dev_err=err)),
         ]
         if mxw:
-            st.append(Stage("gemm_w13_wgrad", "k_gemm_wgrad", 2 * T * 2 * H * D, 0,
-                            lambda: mx.grouped_mm_wgrad(self.dzq["q_col"], self.dzq["s_col"], self.qx["q_col"],
-                                                        self.qx["s_col"], self.offs, out=self.dw13,
-                                                        dev_err=err)))
+            st += [
+                Stage("gemm_w2_wgrad", "k_gemm_wgrad", 2 * T * D * H, 0,
+                      lambda: mx.grouped_mm_wgrad(self.qdy["q_col"], self.qdy["s_col"], self.hq["q_col"],
+                                                  self.hq["s_col"], self.offs, out=self.dw2, dev_err=err)),
+                Stage("gemm_w13_wgrad", "k_gemm_wgrad", 2 * T * 2 * H * D, 0,
+                      lambda: mx.grouped_mm_wgrad(self.dzq["q_col"], self.dzq["s_col"], self.qx["q_col"],
+                                                  self.qx["s_col"], self.offs, out=self.dw13, dev_err=err)),
+            ]
         else:
-            st.append(Stage("gemm_w13_wgrad_hp", "k_gemm_wgrad_hp", 2 * T * 2 * H * D, 0,
-                            lambda: mx.grouped_mm_wgrad_hp(self.dzq["dab"], self.x_pad, self.offs,
-                                                           out=self.dw13, dev_err=err)))
+            st += [
+                Stage("gemm_w2_wgrad_hp", "k_gemm_wgrad_hp", 2 * T * D * H, 0,
+                      lambda: mx.grouped_mm_wgrad_hp(self.dy_pad, self.hq["h"], self.offs, out=self.dw2,
+                                                     dev_err=err)),
+                Stage("gemm_w13_wgrad_hp", "k_gemm_wgrad_hp", 2 * T * 2 * H * D, 0,
+                      lambda: mx.grouped_mm_wgrad_hp(self.dzq["dab"], self.x_pad, self.offs, out=self.dw13,
+                                                     dev_err=err)),
+            ]
+        st.append(Stage("gemm_w13_dgrad", "k_gemm_grouped", 2 * T * 2 * H * D, 0,
+                        lambda: mx.grouped_mm_dgrad_unpad(self.dzq["q_row"], self.dzq["s_row"], self.q13["q_col"],
+                                                          self.q13["s_col"], self.offs, sizes, T, out=self.dx,
+                                                          dev_err=err)))
         return st
 
     def _stages_fp8(self, x, sizes, w13, w2, dy):
@@ -347,20 +351,21 @@ class MoEMLP:
             Stage("gemm_w2_dgrad", "k_gemm_grouped", 2 * T * D * H, 0,
                   lambda: mx.grouped_mm_dgrad(self.qdy["q_row"], self.qdy["s_row"], self.q2["q_col"],
                                               self.q2["s_col"], self.offs, out=self.dh, dev_err=err)),
-            Stage("gemm_w2_wgrad", "k_gemm_wgrad", 2 * T * D * H, 0,
-                  lambda: mx.grouped_mm_wgrad(self.qdy["q_col"], self.qdy["s_col"], self.qh8["q_col"],
-                                              self.qh8["s_col"], self.offs, out=self.dw2, dev_err=err)),
+            # backward in the order described at _stages
             Stage("swiglu_bwd", "k_swiglu_bwd", 0, Tc * H * (6 + 4 * (1 + 1 / 32) + 4),
                   lambda: mx.swiglu_quant_bwd(self.dh, z0, z1, m, want_dab=True, out=self.dzq)),
             Stage("fp8_dz", "k_fp8", 0, _qbytes(Tc * 2 * H, True) + 2 * Tc * 2 * H,
                   lambda: fq(self.dzq["dab"], True, True, offs=self.offs, out=self.qdz8, dev_err=err)),
+            Stage("gemm_w2_wgrad", "k_gemm_wgrad", 2 * T * D * H, 0,
+                  lambda: mx.grouped_mm_wgrad(self.qdy["q_col"], self.qdy["s_col"], self.qh8["q_col"],
+                                              self.qh8["s_col"], self.offs, out=self.dw2, dev_err=err)),
+            Stage("gemm_w13_wgrad", "k_gemm_wgrad", 2 * T * 2 * H * D, 0,
+                  lambda: mx.grouped_mm_wgrad(self.qdz8["q_col"], self.qdz8["s_col"], self.qx["q_col"],
+                                              self.qx["s_col"], self.offs, out=self.dw13, dev_err=err)),
             Stage("gemm_w13_dgrad", "k_gemm_grouped", 2 * T * 2 * H * D, 0,
                   lambda: mx.grouped_mm_dgrad_unpad(self.qdz8["q_row"], self.qdz8["s_row"], self.q13["q_col"],
                                                     self.q13["s_col"], self.offs, sizes, T, out=self.dx,
                                                     dev_err=err)),
-            Stage("gemm_w13_wgrad", "k_gemm_wgrad", 2 * T * 2 * H * D, 0,
-                  lambda: mx.grouped_mm_wgrad(self.qdz8["q_col"], self.qdz8["s_col"], self.qx["q_col"],
-                                              self.qx["s_col"], self.offs, out=self.dw13, dev_err=err)),
         ]
 
     def gemm_flops(self):
