@@ -16,13 +16,14 @@
 // Tile routine: a 256-thread workgroup computes a 256 x 256 output tile in
 // K steps of 128 (four scale blocks, two MFMA K sub-steps). Waves form a
 // 2 x 2 grid, each owning a 128 x 128 sub-tile = 4 x 4 MFMA blocks of
-// 32 x 32 (256 float accumulators per lane, in AGPRs). Operands move global
-// -> LDS by direct DMA (buffer_load ... lds) into two stage buffers (66 KB
-// each): the DMA of step k+1 is issued right after the barrier that opens
-// step k, so it has a whole step to land while step k's operands are read
-// from LDS and its 32 MFMAs run. The two buffers are separate LDS objects and
-// the loop is unrolled twice, so the compiler can tell each DMA from the
-// reads it overlaps. LDS rows are 128 bytes; row r's 16-byte piece p sits in
+// 32 x 32 (256 float accumulators per lane, in AGPRs). Operands reach LDS
+// in two stage buffers (66 KB each), with a barrier in the middle of every
+// step: A's rows and the scales by direct DMA (buffer_load ... lds), issued
+// after the barrier that frees their buffer, so they have a step to land;
+// B's rows through registers, loaded a step before the waves write them to
+// LDS (see step_full). The two buffers are separate LDS objects and the loop
+// is unrolled twice, so the compiler can tell each DMA from the reads it
+// overlaps. LDS rows are 128 bytes; row r's 16-byte piece p sits in
 // slot p ^ f(r) with f(r) = (r & 7) ^ ((r >> 3) & 1). A ds_read_b128 serves
 // 16 lanes (16 consecutive rows, one piece) per pass over the 64 banks
 // (256 bytes): rows of one parity share 128-byte halves, and f takes 8
