@@ -46,11 +46,20 @@ GEMM_SOURCES = ("quantize_grouped_gemm_amd/csrc/mx_gemm.hip", "quantize_grouped_
 
 
 def gemm_source_hash():
+    """Hash of the GEMM kernel's code and build flags. Comments and blank
+    lines of the C++ sources are left out, so editing a comment keeps the
+    counters taken on the same code valid."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in GEMM_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+            text = f.read()
+        if not rel.endswith(".py"):
+            code = re.sub(rb"/\*.*?\*/", b"", text, flags=re.S)
+            code = re.sub(rb"//[^\n]*", b"", code)
+            text = b"\n".join(line.rstrip() for line in code.split(b"\n") if line.strip())
+        h.update(text)
     return h.hexdigest()
 
 
