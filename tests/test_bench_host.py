@@ -67,3 +67,24 @@ def test_source_hash_covers_the_gemm_sources():
     for rel in bench.GEMM_SOURCES:
         assert os.path.isfile(os.path.join(ROOT, rel)), rel
     assert len(bench.gemm_source_hash()) == 64
+
+
+def test_gemm_source_hash_ignores_comments_not_code(tmp_path, monkeypatch):
+    """Counters stay valid across comment edits of the GEMM sources and are
+    dropped when their code changes."""
+    import shutil
+    for rel in bench.GEMM_SOURCES:
+        dst = tmp_path / rel
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(ROOT, rel), dst)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    base = bench.gemm_source_hash()
+    assert base == bench.gemm_source_hash()
+    src = tmp_path / "quantize_grouped_gemm_amd/csrc/mx_gemm.hip"
+    text = src.read_text()
+    src.write_text(text.replace("#include \"mx_device.h\"",
+                                "// a new comment line\n\n#include \"mx_device.h\"  /* and a block comment */", 1))
+    assert bench.gemm_source_hash() == base
+    src.write_text(text.replace("constexpr int kPfOps = 2;", "constexpr int kPfOps = 3;", 1))
+    assert "constexpr int kPfOps = 2;" in text
+    assert bench.gemm_source_hash() != base
