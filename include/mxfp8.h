@@ -284,7 +284,8 @@ mx_status mx_scaled_grouped_mm_dgrad_unpad(const uint8_t* qa, const uint8_t* sa,
  * qx [K, Tcap], sx: X column-wise. Scales in the MX_SCALES_K128 layout.
  * out [E, N, K] (out_dtype); an empty group's slice is written as zeros.
  * N % 16 == 0, K % 16 == 0, Tcap % 128 == 0, Tcap < 2^23 (a tile's 256
- * operand rows of Tcap codes are addressed with 32-bit offsets);
+ * operand rows of Tcap codes are addressed with 32-bit offsets), and
+ * ceil(N/256) * ceil(K/256) * E below 2^31 (one workgroup per tile);
  * MX_ERR_SHAPE otherwise.
  * No workspace: every 256 x 256 tile of dW is computed whole by one
  * workgroup over its group's full token range and written once from

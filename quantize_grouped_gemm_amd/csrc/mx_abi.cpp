@@ -349,6 +349,9 @@ mx_status mx_scaled_grouped_mm_wgrad(const uint8_t* qg, const uint8_t* sg, const
   MX_REQUIRE(Tcap >= 0 && Tcap % 128 == 0, MX_ERR_SHAPE, "%s: Tcap must be a multiple of 128", fn);
   MX_REQUIRE(N > 0 && N % 16 == 0 && K > 0 && K % 16 == 0, MX_ERR_SHAPE, "%s: N and K must be positive multiples of 16", fn);
   MX_REQUIRE((N + 255) / 256 <= 65535 && (K + 255) / 256 <= 65535, MX_ERR_SHAPE, "%s: too large", fn);
+  // one workgroup per 256 x 256 tile of every group's dW, in a 1-D grid
+  MX_REQUIRE((N + 255) / 256 * ((K + 255) / 256) * E <= 0x7FFFFFFF, MX_ERR_SHAPE,
+             "%s: too many tiles for one launch", fn);
   MX_REQUIRE(scales_fit(N, Tcap) && scales_fit(K, Tcap), MX_ERR_SHAPE, "%s: scale matrices too large", fn);
   MX_REQUIRE(Tcap * 256 < (1ll << 31), MX_ERR_SHAPE,
              "%s: Tcap (%lld) must be below 2^23: a tile's 256 operand rows are addressed with 32-bit offsets", fn,

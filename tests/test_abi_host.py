@@ -73,6 +73,9 @@ def test_argument_errors_are_reported_without_device_work():
     # MXFP8 weight gradient: 256 rows of Tcap codes must be addressable with 32-bit offsets
     st = L.mx_scaled_grouped_mm_wgrad(p, p, p, p, p, 4, 1 << 23, 16, 16, 1, p, None, None)
     assert st == 2 and b"below 2^23" in L.mx_last_error()
+    # one workgroup per dW tile of every group: the 1-D grid must hold them
+    st = L.mx_scaled_grouped_mm_wgrad(p, p, p, p, p, 1024, 128, 1 << 20, 1 << 20, 0, p, None, None)
+    assert st == 2 and b"too many tiles" in L.mx_last_error()
     assert L.mx_pad_groups(p, p, 2, 10, 24, 128, 256, p, p, p, None, None) == 2
     assert L.mx_unpad_groups(p, p, 128, 10, 32, None, None) == 1
     # FP8 row-scaled: cols not a multiple of 128; column-wise rows not a
