@@ -269,6 +269,11 @@ def test_abi_rejects_bad_arguments(gpu):
         mx.scaled_mm(q, s, q, s)                                  # K = 96 not a multiple of 128
     with pytest.raises(mx.MXError):
         mx.quantize(torch.zeros((64, 48), dtype=torch.bfloat16, device=dev()))   # cols % 32
+    x = torch.zeros((64, 136), dtype=torch.bfloat16, device=dev())
+    with pytest.raises(mx.MXError, match="16-byte aligned"):
+        mx.quantize(x[:, 4:132])                                  # rows start 8 bytes into a 16-byte unit
+    with pytest.raises(mx.MXError, match="q_row: "):              # output smaller than the sizes passed
+        mx.quantize(x[:, :128], out={"q_row": torch.empty((64, 96), dtype=torch.uint8, device=dev())})
 
 
 # ---------------------------------------------------------------- full shapes
