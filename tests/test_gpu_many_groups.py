@@ -148,3 +148,45 @@ def test_bad_offsets_flag_dev_err_both_tables(gpu, E):
                 mx.grouped_mm_wgrad(*_mx_dev(qg, sg), *_mx_dev(qx, sx), to_dev(offs), torch.float32, dev_err=err)
             torch.cuda.synchronize()
             assert (int(err.item()) & 1) == want, (run, offs.tolist())
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_bit_exact(gpu, seed):
+    """Seeded random shapes around the tile edges: 1..80 groups (empty ones
+    included, so both group tables run), N and the weight gradient's K any
+    multiple of 16 up to 640 (partial column tiles), K 128..640 (one to five
+    K steps, odd counts included), a tail of 0..2 slots. Forward, dgrad,
+    weight gradient and the token-order forward, bit for bit against the
+    oracle on exact operands."""
+    rng = np.random.default_rng(1000 + seed)
+    E = int(rng.integers(1, 81))
+    N = 16 * int(rng.integers(1, 41))
+    K = 128 * int(rng.integers(1, 6))
+    Kw = 16 * int(rng.integers(1, 41))
+    offs = np.cumsum(_slots(E, 2000 + seed, float(rng.uniform(0.0, 0.6)))).astype(np.int32)
+    Tcap = int(offs[-1]) + 128 * int(rng.integers(0, 3))
+    print(f"seed {seed}: E={E} N={N} K={K} Kw={Kw} Tcap={Tcap}", flush=True)
+    qa, sa = _int_mx((Tcap, K), 3 * seed)
+    qw, sw = _int_mx((E, N, K), 3 * seed + 1)
+    ref = O.grouped_mm(qa, sa, qw, sw, offs)
+    err = torch.zeros(1, dtype=torch.int32, device=dev())
+    for fn in (mx.grouped_mm_fwd, mx.grouped_mm_dgrad):
+        out = torch.full((Tcap, N), float("nan"), dtype=torch.float32, device=dev())
+        got = fn(*_mx_dev(qa, sa), *_mx_dev(qw, sw), to_dev(offs), torch.float32, out=out, dev_err=err)
+        np.testing.assert_array_equal(host(got).astype(np.float64), ref, err_msg=fn.__name__)
+    # token order: each group's first n_g padded rows are its tokens
+    slot = np.diff(np.concatenate([[0], offs]))
+    sizes = np.minimum(slot, rng.integers(0, 129, E) + np.maximum(slot - 128, 0)).astype(np.int32)
+    T = int(sizes.sum())
+    if T:
+        rows = np.concatenate([np.arange(s, s + n) for s, n in zip(offs - slot, sizes)]).astype(np.int64)
+        got_t = mx.grouped_mm_fwd_unpad(*_mx_dev(qa, sa), *_mx_dev(qw, sw), to_dev(offs), to_dev(sizes), T,
+                                        torch.float32, dev_err=err)
+        np.testing.assert_array_equal(host(got_t).astype(np.float64), ref[rows])
+    qg, sg = _int_mx((N, Tcap), 3 * seed + 2)
+    qx, sx = _int_mx((Kw, Tcap), 3 * seed + 3)
+    out = torch.full((E, N, Kw), float("nan"), dtype=torch.float32, device=dev())
+    got = mx.grouped_mm_wgrad(*_mx_dev(qg, sg), *_mx_dev(qx, sx), to_dev(offs), torch.float32, out=out,
+                              dev_err=err)
+    np.testing.assert_array_equal(host(got).astype(np.float64), O.grouped_mm_wgrad(qg, sg, qx, sx, offs))
+    assert int(err.item()) == 0
