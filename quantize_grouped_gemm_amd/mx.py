@@ -384,7 +384,9 @@ def scaled_mm(qa, sa, qb, sb, out_dtype=torch.bfloat16, out=None):
     _want(sb, "sb", torch.uint8, N * K // 32)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
-    _want_out(out, "out", shape=(M, N))
+    if not isinstance(out, torch.Tensor) or out.dtype not in (torch.bfloat16, torch.float32):
+        raise MXError("out: expected a tensor of torch.bfloat16, torch.float32")
+    _want_rows(out, "out", out.dtype, (M, N))   # rows may be spaced wider (ld_out)
     _device(qa, sa, qb, sb, out)
     st = lib().mx_scaled_mm(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), M, N, K, _DT[out.dtype],
                             _ptr(out), out.stride(0), _stream(qa.device))

@@ -36,6 +36,9 @@ def test_dense_gemm_buffers():
     raises(mx.scaled_mm, qa, sa, qb, sb, out=torch.zeros((M, N + 16), dtype=BF), match="out: shape")
     raises(mx.scaled_mm, qa, sa, qb, sb, out=torch.zeros((M, N), dtype=torch.float16), match="out: expected")
     raises(mx.scaled_mm, u8(M, 2 * K)[:, :K], sa, qb, sb, match="qa must be contiguous")
+    raises(mx.scaled_mm, qa, sa, qb, sb, out=torch.zeros((N, M), dtype=BF).t(), match="contiguous rows")
+    # an output whose rows are spaced wider than N is accepted up to the device check
+    raises(mx.scaled_mm, qa, sa, qb, sb, out=torch.zeros((M, N + 32), dtype=BF)[:, :N], match="cuda")
     raises(mx.scaled_mm, qa.to(torch.int8), sa, qb, sb, match="qa: dtype")
     # matching buffers reach the device check, not the library
     raises(mx.scaled_mm, qa, sa, qb, sb, match="cuda")

@@ -62,6 +62,25 @@ def test_scaled_mm_exact_with_scales(gpu, M, N, K):
     np.testing.assert_array_equal(host(got).astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_scaled_mm_random_shapes_exact(gpu, seed):
+    """Seeded random shapes around the tile edges (M any, N a multiple of 16,
+    K one to six 128-wide steps), written into a wider output (row stride
+    above N): exact operands, bit for bit, and the columns past N untouched."""
+    rng = np.random.default_rng(3000 + seed)
+    M = int(rng.integers(1, 700))
+    N = 16 * int(rng.integers(1, 45))
+    K = 128 * int(rng.integers(1, 7))
+    ld = N + 16 * int(rng.integers(0, 3))
+    print(f"seed {seed}: M={M} N={N} K={K} ld={ld}", flush=True)
+    qa, sa = _int_mx((M, K), 2 * seed)
+    qb, sb = _int_mx((N, K), 2 * seed + 1)
+    wide = torch.full((M, ld), 7.0, dtype=torch.float32, device=dev())
+    got = mx.scaled_mm(*_mx_dev(qa, sa), *_mx_dev(qb, sb), out=wide[:, :N])
+    np.testing.assert_array_equal(host(got).astype(np.float64), O.scaled_mm(qa, sa, qb, sb))
+    assert torch.all(wide[:, N:] == 7.0)
+
+
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("M,N,K", [(256, 256, 512), (300, 200, 384), (512, 768, 1024), (16, 48, 128)])
 def test_scaled_mm_realistic(gpu, M, N, K, out_dtype):

@@ -43,6 +43,37 @@ def test_quantize_shapes_k128(gpu, mode, shape):
     _check_quant(xb, to_dev(xb.view(np.int16)).view(torch.bfloat16), mode, layout="k128")
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_quantize_random_shapes(gpu, seed):
+    """Seeded random requests: batch of 1..3 matrices, row stride wider than
+    the columns, either scale layout, mode and direction set, sizes off the
+    128 x 128 tile grid where the layout allows (row-wise: any row count;
+    plain scales: columns and column-wise rows in multiples of 32)."""
+    rng = np.random.default_rng(4000 + seed)
+    layout = ["plain", "k128"][seed % 2]
+    mode = MODES[int(rng.integers(0, 2))]
+    rowwise, colwise = [(True, False), (False, True), (True, True)][int(rng.integers(0, 3))]
+    m = 128 if layout == "k128" else 32
+    C = m * int(rng.integers(1, 1 + 640 // m))
+    R = (m if colwise else 1) * int(rng.integers(1, 1 + 640 // (m if colwise else 1)))
+    batch = int(rng.integers(1, 4))
+    ld = C + 8 * int(rng.integers(0, 5))
+    print(f"seed {seed}: {layout} {mode} row={rowwise} col={colwise} batch={batch} R={R} C={C} ld={ld}", flush=True)
+    xb = synth.bits(synth.normal_bf16((batch, R, ld), 1.0, synth.generator(seed)))
+    # a few blocks at large and tiny magnitudes
+    xb[:, : R // 2, : min(C, 64)] = synth.bits(
+        synth.normal_bf16((batch, R // 2, min(C, 64)), 2.0 ** 12, synth.generator(seed + 50)))
+    xt = to_dev(xb.view(np.int16)).view(torch.bfloat16)[..., :C]
+    got = mx.quantize(xt, mode, rowwise, colwise, layout=layout)
+    for b in range(batch):
+        ref = O.quantize_bf16(np.ascontiguousarray(xb[b, :, :C]), mode, rowwise, colwise)
+        for k in ref:
+            g = host(got[k][b])
+            if k.startswith("s_") and layout == "k128":
+                g = plain(g)
+            np.testing.assert_array_equal(g, ref[k], err_msg=f"{k} matrix {b}")
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_quantize_rowwise_any_rows_and_separate_directions(gpu, mode):
     xb = synth.bits(synth.normal_bf16((100, 96), 1.0, synth.generator(3)))
