@@ -78,6 +78,44 @@ def test_swiglu_bwd(gpu, mode, T, H, layout):
         assert torch.equal(st[k], got[k]), k
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_swiglu_random_shapes(gpu, seed):
+    """Seeded random shapes off the tile grid (T and H multiples of 32, or of
+    128 for k128 scales), a and b with a row stride wider than 2H (views of
+    a wider z), dh with its own wider stride: forward and backward against
+    the oracle, and the fused-vs-standalone bytes."""
+    rng = np.random.default_rng(5000 + seed)
+    layout = ["plain", "k128"][seed % 2]
+    mode = ["rceil", "floor"][int(rng.integers(0, 2))]
+    m = 128 if layout == "k128" else 32
+    T = m * int(rng.integers(1, 1 + 512 // m))
+    H = m * int(rng.integers(1, 1 + 512 // m))
+    pad_z = 8 * int(rng.integers(0, 4))
+    pad_dh = 8 * int(rng.integers(0, 4))
+    print(f"seed {seed}: {layout} {mode} T={T} H={H} pad_z={pad_z} pad_dh={pad_dh}", flush=True)
+    g = synth.generator(6000 + seed)
+    zb = synth.bits(synth.normal_bf16((T, 2 * H + pad_z), 2.0, g))
+    dhb = synth.bits(synth.normal_bf16((T, H + pad_dh), 1.0, g))
+    z = _dev_bf16(zb)
+    dh = _dev_bf16(dhb)[:, :H]
+    za, zbb = zb[:, :H], zb[:, H:2 * H]
+    got = mx.swiglu_quant_fwd(z[:, :H], z[:, H:2 * H], mode, want_h=True, layout=layout)
+    ref = O.swiglu_quant_fwd(np.ascontiguousarray(za), np.ascontiguousarray(zbb), mode)
+    _assert_close_codes((host(got["q_row"]), _scales(got["s_row"], layout)), (ref["q_row"], ref["s_row"]), "fwd row")
+    _assert_close_codes((host(got["q_col"]), _scales(got["s_col"], layout)), (ref["q_col"], ref["s_col"]), "fwd col")
+    st = mx.quantize(got["h"], mode, True, True, layout=layout)
+    for k in ("q_row", "s_row", "q_col", "s_col"):
+        assert torch.equal(st[k], got[k]), k
+    got = mx.swiglu_quant_bwd(dh, z[:, :H], z[:, H:2 * H], mode, want_dab=True, layout=layout)
+    ref = O.swiglu_quant_bwd(np.ascontiguousarray(dhb[:, :H]), np.ascontiguousarray(za), np.ascontiguousarray(zbb),
+                             mode)
+    _assert_close_codes((host(got["q_row"]), _scales(got["s_row"], layout)), (ref["q_row"], ref["s_row"]), "bwd row")
+    _assert_close_codes((host(got["q_col"]), _scales(got["s_col"], layout)), (ref["q_col"], ref["s_col"]), "bwd col")
+    st = mx.quantize(got["dab"], mode, True, True, layout=layout)
+    for k in ("q_row", "s_row", "q_col", "s_col"):
+        assert torch.equal(st[k], got[k]), k
+
+
 def test_swiglu_special_values(gpu):
     """Zero gate or up halves give exact zeros; large |a| saturates silu."""
     T, H = 64, 64
