@@ -190,3 +190,26 @@ def test_random_shapes_bit_exact(gpu, seed):
                               dev_err=err)
     np.testing.assert_array_equal(host(got).astype(np.float64), O.grouped_mm_wgrad(qg, sg, qx, sx, offs))
     assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shapes_wgrad_hp(gpu, seed):
+    """wgrad_with_hp on seeded random shapes: 1..80 groups, N and K any
+    multiple of 16 up to 640, a tail of 0..2 slots; small-integer bf16
+    operands, so the float32 sums are exact and the one bf16 rounding must
+    match the oracle's bit for bit."""
+    rng = np.random.default_rng(7000 + seed)
+    E = int(rng.integers(1, 81))
+    N = 16 * int(rng.integers(1, 41))
+    K = 16 * int(rng.integers(1, 41))
+    offs = np.cumsum(_slots(E, 8000 + seed, float(rng.uniform(0.0, 0.6)))).astype(np.int32)
+    Tcap = int(offs[-1]) + 128 * int(rng.integers(0, 3))
+    print(f"seed {seed}: E={E} N={N} K={K} Tcap={Tcap}", flush=True)
+    g = torch.from_numpy(rng.integers(-8, 9, (Tcap, N)).astype(np.float32)).to(torch.bfloat16)
+    x = torch.from_numpy(rng.integers(-8, 9, (Tcap, K)).astype(np.float32)).to(torch.bfloat16)
+    out = torch.full((E, N, K), float("nan"), dtype=torch.bfloat16, device=dev())
+    err = torch.zeros(1, dtype=torch.int32, device=dev())
+    got = mx.grouped_mm_wgrad_hp(g.to(dev()), x.to(dev()), to_dev(offs), out=out, dev_err=err)
+    ref = O.grouped_mm_wgrad_hp(synth.bits(g), synth.bits(x), offs)
+    np.testing.assert_array_equal(bf16_host(got).view(np.uint16), O.f64_to_bf16(ref))
+    assert int(err.item()) == 0
