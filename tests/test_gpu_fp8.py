@@ -80,6 +80,45 @@ def test_fp8_dual(gpu, shape, slots):
     np.testing.assert_array_equal(plain(host(got["s_col"])), ref["s_col"])
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_fp8_random_shapes(gpu, seed):
+    """Seeded random requests for the three FP8 entry points: batch of 1..2
+    matrices, rows and columns multiples of 128 up to 1024 (row-wise rows:
+    any count), a row stride wider than the columns, per-group column
+    scales over random segments (empty ones included) or none."""
+    rng = np.random.default_rng(9000 + seed)
+    batch = 2 if seed % 3 == 0 else 1
+    R = 128 * int(rng.integers(1, 9))
+    C = 128 * int(rng.integers(1, 9))
+    ld = C + 8 * int(rng.integers(0, 4))
+    slots = None
+    if batch == 1 and rng.random() < 0.6:
+        n = int(rng.integers(1, 6))
+        parts = np.sort(rng.integers(0, R // 128 + 1, n - 1))
+        slots = np.diff(np.concatenate([[0], parts, [R // 128 - int(rng.integers(0, 2))]])) * 128
+        slots = np.maximum(slots, 0)
+    print(f"seed {seed}: batch={batch} R={R} C={C} ld={ld} slots={None if slots is None else list(slots)}",
+          flush=True)
+    full = _inputs((batch, R, ld), 9100 + seed)
+    b = np.ascontiguousarray(full[..., :C])
+    x = _bf16_dev(full)[..., :C]
+    if batch == 1:
+        b, x = b[0], x[0]
+    offs = None if slots is None else np.cumsum(slots).astype(np.int32)
+    offs_d = None if offs is None else to_dev(offs)
+    err = torch.zeros(1, dtype=torch.int32, device=dev())
+    got = mx.quantize_fp8(x, rowwise=True, colwise=True, offs=offs_d, dev_err=err)
+    sep = mx.quantize_fp8(x, rowwise=True, colwise=True, offs=offs_d, fused=False, dev_err=err)
+    ref = O.quantize_fp8_bf16(b, rowwise=True, colwise=True, segments=offs)
+    for k in ("q_row", "s_row", "q_col", "s_col"):
+        assert torch.equal(got[k], sep[k]), k
+    np.testing.assert_array_equal(host(got["q_row"]), ref["q_row"])
+    np.testing.assert_array_equal(plain(host(got["s_row"])), ref["s_row"])
+    np.testing.assert_array_equal(host(got["q_col"]), ref["q_col"])
+    np.testing.assert_array_equal(plain(host(got["s_col"])), ref["s_col"])
+    assert int(err.item()) == 0
+
+
 def test_fp8_grouped_gemms_through_the_mx_kernels(gpu):
     """Forward and weight gradient on FP8 row-scaled operands: the MXFP8
     grouped kernels against the oracle's float64 GEMM of the dequantized
