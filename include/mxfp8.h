@@ -39,14 +39,18 @@
  *  - `stream` is a hipStream_t (NULL = the null stream). Every call only
  *    enqueues work on it: no call synchronizes, and no call reads device
  *    memory on the host, so calls can be captured in a HIP graph.
- *  - Device pointers must be 16-byte aligned; leading dimensions are given in
- *    elements and must keep every row 16-byte aligned.
+ *  - Pointers to bf16 data, E4M3 codes and GEMM outputs must be 16-byte
+ *    aligned; scale pointers 4-byte aligned in the MX_SCALES_K128 layout
+ *    (any alignment in MX_SCALES_PLAIN); int32 arrays 4-byte aligned.
+ *    Leading dimensions are given in elements and must keep every row
+ *    16-byte aligned.
  *  - Errors: every argument is checked on the host before anything is
  *    enqueued. A non-zero status means nothing was enqueued; mx_last_error()
  *    then returns a message for the calling thread. There is no fallback path:
  *    if the library cannot run a call on the current device it fails.
- *  - Grouped calls take per-group offsets in device memory (int32 [E],
- *    exclusive ends: group g owns rows [offs[g-1], offs[g]) with offs[-1] = 0).
+ *  - Grouped calls take 1 <= E <= 1024 groups (MX_ERR_SHAPE otherwise) and
+ *    per-group offsets in device memory (int32 [E], exclusive ends: group g
+ *    owns rows [offs[g-1], offs[g]) with offs[-1] = 0).
  *    Offsets are never read on the host. Kernels check them on the device:
  *    they must be non-decreasing multiples of 128 no larger than the padded
  *    capacity Tcap. If they are not and `dev_err` is non-NULL, bit 0 of
@@ -181,8 +185,9 @@ mx_status mx_swiglu_quant_bwd(const void* dh, int64_t ld_dh, const void* a,
  * contiguous run. Scales written in MX_SCALES_PLAIN must be re-quantized (or
  * permuted) into MX_SCALES_K128 before they are passed to a GEMM; the GEMMs
  * cannot tell the layouts apart and would read wrong scales.
- * out row stride ld_out elements (>= N). K % 128 == 0, K < 2^23 (a tile's
- * 256 operand rows are addressed with 32-bit offsets); M, N >= 1.
+ * out row stride ld_out elements (>= N, rows 16-byte aligned). K % 128 == 0,
+ * K < 2^23 (a tile's 256 operand rows are addressed with 32-bit offsets);
+ * M, N >= 0 (an empty output enqueues nothing).
  * The same call serves the forward, the input gradient (A = dY row-wise,
  * B = W column-wise) and the weight gradient (A = dY column-wise, B = X
  * column-wise). */
