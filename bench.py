@@ -6,11 +6,12 @@ Default workload: one training step (forward + backward) of the routed-
 experts MXFP8 SwiGLU MLP at one GPU's share of a Llama4-Scout-like MoE
 (16 experts, dim 5120, expert hidden 8192, 16384 top-1 tokens with Zipf(1.1)
 group sizes, two experts empty, groups padded to 128). A step runs every
-kernel of the path: group padding, MX quantization of activations and both
-weights (row- and column-wise), grouped MXFP8 GEMMs (forward, input and
-weight gradients), the fused SwiGLU + dual quantization boundary forward and
-backward, and unpadding. Inputs are seeded synthetic tensors resident in HBM
-before timing starts.
+kernel of the path: MX quantization of the activations (with the group
+padding fused in) and of both weights (row- and column-wise), grouped MXFP8
+GEMMs (forward, input and weight gradients; the two that produce y and dx
+write token order, so unpadding is fused in), and the fused SwiGLU + dual
+quantization boundary forward and backward. Inputs are seeded synthetic
+tensors resident in HBM before timing starts.
 
 Prints one JSON line. `value` is tokens per second of the whole step;
 `roofline` is for the dominant kernel (the grouped MXFP8 GEMM), with its
