@@ -3,8 +3,9 @@
 // 32-element K block of each operand row, float32 accumulation).
 //
 // Every GEMM here is C[m, n] = sum_k A[m, k] B[n, k], both operands row-major
-// with K contiguous, scales [rows, K/32]. Three kernels share one tile
-// routine:
+// with K contiguous, block scales in the K128 layout [K/128, rows, 4] (the
+// four block scales of a row's 128-wide K step form one dword, rows
+// contiguous). Three kernels share one tile routine:
 //   k_gemm_dense    one matrix pair (the linear layer's fwd / dgrad / wgrad)
 //   k_gemm_grouped  2-D x 3-D: row tiles of A belong to one expert group and
 //                   multiply that expert's B (grouped fwd and dgrad)
@@ -75,7 +76,7 @@ struct TileOrder {
 constexpr TileOrder kOrderDense{4, 16, 4};
 constexpr TileOrder kOrderGrouped{2, 16, 8};
 constexpr TileOrder kOrderWgrad{3, 0, 4};
-constexpr int kMaxGroups = 1024;                         // group table lives in LDS
+constexpr int kMaxGroups = 1024;                         // from 64 groups on, the table lives in LDS
 // vector-memory ops per wave and K step of the MXFP8 loop:
 constexpr int kDmaOpsA = 10;   // A and the scales by DMA
 constexpr int kBLoads = 8;     // B's rows by plain loads (see load_b_regs)
